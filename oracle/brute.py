@@ -1,0 +1,54 @@
+"""Scalar pure-Python attention for tiny inputs (test infrastructure only).
+
+The same definition as ``oracle.attention`` written with nested loops over
+Python floats, ``math.exp``, ``math.log`` and ``math.fsum``: no numpy, no
+matrix products, no vectorised masking.  It shares no helper with the numpy
+oracle, so the two agreeing to 1e-12 pins the numpy version's indexing (head
+grouping, transposes, bias sign and offset, visibility) on every shape small
+enough to run here (sequence lengths up to about 8).
+"""
+from __future__ import annotations
+
+import math
+
+
+def attention(q, k, v, scale, causal=False, key_padding_mask=None,
+              alibi_slopes=None):
+    """q: nested ``[B][S_q][H_q][D]``; k, v: ``[B][S_k][H_kv][D]``.
+
+    Returns ``(out [B][S_q][H_q][D], lse [B][H_q][S_q])`` as Python floats.
+    """
+    B, S_q, H_q, D = len(q), len(q[0]), len(q[0][0]), len(q[0][0][0])
+    S_k, H_kv = len(k[0]), len(k[0][0])
+    G = H_q // H_kv
+    out = [[[[0.0] * D for _ in range(H_q)] for _ in range(S_q)] for _ in range(B)]
+    lse = [[[float("-inf")] * S_q for _ in range(H_q)] for _ in range(B)]
+    for b in range(B):
+        for h in range(H_q):
+            hk = h // G
+            for i in range(S_q):
+                pos = i + S_k - S_q
+                keys, scores = [], []
+                for j in range(S_k):
+                    if causal and j > pos:
+                        continue
+                    if key_padding_mask is not None and not key_padding_mask[b][j]:
+                        continue
+                    dot = math.fsum(float(q[b][i][h][d]) * float(k[b][j][hk][d])
+                                    for d in range(D))
+                    sc = float(scale) * dot
+                    if alibi_slopes is not None:
+                        sc -= float(alibi_slopes[h]) * abs(pos - j)
+                    keys.append(j)
+                    scores.append(sc)
+                if not keys:
+                    continue
+                top = max(scores)
+                total = math.fsum(math.exp(x - top) for x in scores)
+                row_lse = top + math.log(total)
+                lse[b][h][i] = row_lse
+                for d in range(D):
+                    out[b][i][h][d] = math.fsum(
+                        math.exp(sc - row_lse) * float(v[b][j][hk][d])
+                        for sc, j in zip(scores, keys))
+    return out, lse
