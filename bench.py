@@ -1,0 +1,270 @@
+#!/usr/bin/env python3
+"""Benchmark of the streaming-attention hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+
+A step is one pass of the whole hot path over resident synthetic inputs:
+
+* the prefill forward on the 2 x 8192 x 32 x 128 bf16 causal workload with
+  ALiBi and a random padding tail (every prefill step: Q tile, K/V streaming,
+  scores, bias and masks, online softmax, output and lse), then
+* the GQA decode (split-KV + log-sum-exp merge) of 4 sequences over a 32768
+  key cache, 14 query heads on 2 KV heads, D = 64, fp16.  Decode steps rotate
+  over 8 distinct caches (512 MiB) so the 256 MB last-level cache cannot serve
+  one step from the previous one.
+
+``value`` is the step's algorithmic FLOPs (4 * D * H_q * visible query-key
+pairs, summed over the parts) divided by the measured time per step, in
+TFLOP/s.  HIP events recorded on the launch stream time each part; the
+``roofline`` object is for the dominant kernel (the prefill kernel) against
+the 2.5 PFLOP/s dense bf16 matrix peak, and ``decode`` carries the decode
+part's key/value read bandwidth against 8 TB/s.  ``cpu_baseline`` times the
+float64 CPU oracle on a bounded sample of the same workloads on this host.
+
+Prints one JSON line on stdout.  Only one GPU is supported: --gpus above 1
+exits with a message.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+from pathlib import Path
+
+ROOT = Path(__file__).resolve().parent
+sys.path.insert(0, str(ROOT))
+
+METRIC = "prefill fwd TFLOP/s + decode KV HBM GB/s, each as % of MI355X roofline"
+MFMA_PEAK_TFLOPS = 2500.0   # MI355X dense fp16/bf16 matrix peak (published)
+HBM_PEAK_GBS = 8000.0       # MI355X HBM3E bandwidth (published)
+DECODE_ROTATION = 8
+PROFILES = ROOT / "profiles"
+KERNEL_SOURCES = ["common.hpp", "prefill.hpp", "decode.hpp", "sa_attn.hip"]
+
+STEPS = {
+    "c5+c4": ["c5_alibi_8192", "c4_decode_32k"],
+    "c3_causal_4096": ["c3_causal_4096"],
+    "c3_noncausal_4096": ["c3_noncausal_4096"],
+    "c5_alibi_8192": ["c5_alibi_8192"],
+    "c4_decode_32k": ["c4_decode_32k"],
+    "c2_causal_pad16": ["c2_causal_pad16"],
+    "c1_fwd_256": ["c1_fwd_256"],
+}
+
+
+def visible_pairs(w, tails):
+    """Query-key pairs the method must visit (causal rule and padding tails)."""
+    import numpy as np
+    total = 0
+    i = np.arange(w.S_q, dtype=np.int64)
+    for b in range(w.B):
+        t = tails[b] if tails else 0
+        last_valid = w.S_k - t - 1
+        last = i + (w.S_k - w.S_q) if w.causal else np.full_like(i, w.S_k - 1)
+        last = np.minimum(last, last_valid)
+        total += int(np.clip(last + 1, 0, None).sum())
+    return total
+
+
+def algorithmic_flops(w, tails):
+    return 4 * w.D * w.H_q * visible_pairs(w, tails)
+
+
+def kv_bytes(w):
+    return 2 * w.B * w.S_k * w.H_kv * w.D * 2
+
+
+def source_sha():
+    h = hashlib.sha256()
+    for n in KERNEL_SOURCES:
+        h.update((ROOT / "online_softmax_amd" / "csrc" / n).read_bytes())
+    return h.hexdigest()[:16]
+
+
+def read_traffic(kernel, workload):
+    """HBM bytes per launch from a committed counter summary, if still current."""
+    p = PROFILES / f"{kernel}_{workload}_traffic.txt"
+    if not p.exists():
+        return None
+    kv = {}
+    for line in p.read_text().splitlines():
+        if ":" in line and not line.startswith("#"):
+            a, b = line.split(":", 1)
+            kv[a.strip()] = b.strip()
+    if kv.get("kernel_source_sha") != source_sha():
+        return None
+    try:
+        return float(kv["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+class Part:
+    def __init__(self, name, dev):
+        import torch
+        import online_softmax_amd as sa
+        from workloads import WORKLOADS, make_inputs
+        self.w = w = WORKLOADS[name]
+        self.sa = sa
+        inp = make_inputs(w)
+        self.tails = inp.tails
+        d = lambda t: None if t is None else t.to(dev)
+        self.q, self.mask, self.slopes = d(inp.q), d(inp.mask), d(inp.slopes)
+        if w.decode:
+            self.ks = [d(inp.k)] + [d(inp.k).clone() for _ in range(DECODE_ROTATION - 1)]
+            self.vs = [d(inp.v)] + [d(inp.v).clone() for _ in range(DECODE_ROTATION - 1)]
+            self.ws = sa.decode_workspace(w.B, w.H_q, w.S_k, w.D, dev)
+            self.lse = torch.empty((w.B, w.H_q, 1), dtype=torch.float32, device=dev)
+        else:
+            self.ks, self.vs = [d(inp.k)], [d(inp.v)]
+            self.lse = torch.empty((w.B, w.H_q, w.S_q), dtype=torch.float32, device=dev)
+        self.out = torch.empty_like(self.q)
+        self.flops = algorithmic_flops(w, self.tails)
+        self.calls = 0
+        del inp
+
+    def run(self):
+        w, i = self.w, self.calls % len(self.ks)
+        self.calls += 1
+        if w.decode:
+            self.sa.attn_decode(self.q, self.ks[i], self.vs[i], scale=w.scale,
+                                key_padding_mask=self.mask, alibi_slopes=self.slopes,
+                                out=self.out, lse=self.lse, workspace=self.ws)
+        else:
+            self.sa.attn_fwd(self.q, self.ks[i], self.vs[i], causal=w.causal, scale=w.scale,
+                             key_padding_mask=self.mask, alibi_slopes=self.slopes,
+                             out=self.out, lse=self.lse)
+
+
+def cpu_baseline(parts, budget_s):
+    """Float64 oracle on a bounded row sample of each part, on this host's cores."""
+    import numpy as np
+    import oracle
+    from workloads import make_inputs, to_f64
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    except Exception:
+        threads = os.cpu_count() or 1
+    flops = 0
+    secs = 0.0
+    samples = []
+    per_part = budget_s / len(parts)
+    for p in parts:
+        w = p.w
+        inp = make_inputs(w)
+        q, k, v = to_f64(inp.q), to_f64(inp.k), to_f64(inp.v)
+        mask = None if inp.mask is None else inp.mask.numpy()
+        sl = None if inp.slopes is None else inp.slopes.numpy()
+        causal = w.causal and not w.decode
+        # Grow an evenly spaced row sample until the part has used its budget.
+        n_rows, used, done_rows = 1, 0.0, 0
+        while used < per_part and done_rows < w.S_q:
+            n = min(n_rows, w.S_q - done_rows)
+            rows = (np.arange(done_rows, done_rows + n) * 7919) % w.S_q
+            t0 = time.perf_counter()
+            oracle.attention(q, k, v, w.scale, causal=causal, key_padding_mask=mask,
+                             alibi_slopes=sl, rows=rows)
+            used += time.perf_counter() - t0
+            for b in range(w.B):
+                t = inp.tails[b] if inp.tails else 0
+                lastv = w.S_k - t - 1
+                last = rows + (w.S_k - w.S_q) if causal else np.full(len(rows), w.S_k - 1)
+                flops += 4 * w.D * w.H_q * int(np.clip(np.minimum(last, lastv) + 1, 0, None).sum())
+            done_rows += n
+            n_rows *= 2
+        secs += used
+        samples.append(f"{w.name}: {done_rows} of {w.S_q} query rows x all batches and heads")
+    return {"value": flops / secs / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": "; ".join(samples) + f" ({secs:.1f} s of float64 numpy)"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="c5+c4", choices=sorted(STEPS))
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=15.0)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on exactly one GPU (asked for {args.gpus}); multi-GPU sharding is "
+              "not part of this build.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    assert torch.cuda.is_available(), "no GPU visible"
+    dev = torch.device("cuda:0")
+    parts = [Part(n, dev) for n in STEPS[args.workload]]
+    stream = torch.cuda.current_stream(dev)
+
+    for _ in range(args.warmup):
+        for p in parts:
+            p.run()
+    torch.cuda.synchronize()
+
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(parts) + 1)] for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        ev[s][0].record(stream)
+        for i, p in enumerate(parts):
+            p.run()
+            ev[s][i + 1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    part_ms = [sum(ev[s][i].elapsed_time(ev[s][i + 1]) for s in range(args.steps)) / args.steps
+               for i in range(len(parts))]
+    step_ms = sum(ev[s][0].elapsed_time(ev[s][-1]) for s in range(args.steps)) / args.steps
+    ms_per_step = max(step_ms, 0.0)
+
+    total_flops = sum(p.flops for p in parts)
+    value = total_flops / (ms_per_step * 1e-3) / 1e12
+
+    result = {
+        "metric": METRIC, "value": round(value, 3), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": parts[0].w.dtype if parts[0].w.dtype != "fp16" else "fp16",
+        "data": "synthetic (seeded N(0,1) q/k/v)",
+        "config": {"workload": args.workload,
+                   "parts": [f"{p.w.name}: B={p.w.B} S_q={p.w.S_q} S_k={p.w.S_k} H_q={p.w.H_q} "
+                             f"H_kv={p.w.H_kv} D={p.w.D} {p.w.dtype} causal={p.w.causal} "
+                             f"mask={'tails ' + str(p.tails) if p.tails else 'none'} "
+                             f"alibi={p.w.alibi}" for p in parts],
+                   "wall_s_timed_region": round(wall, 4)},
+    }
+    prefill = [(p, t) for p, t in zip(parts, part_ms) if not p.w.decode]
+    decode = [(p, t) for p, t in zip(parts, part_ms) if p.w.decode]
+    if prefill:
+        p, t = max(prefill, key=lambda x: x[1])
+        ach = p.flops / (t * 1e-3) / 1e12
+        result["roofline"] = {"bound": "mfma", "achieved": round(ach, 2), "peak": MFMA_PEAK_TFLOPS,
+                              "unit": "TFLOP/s", "frac": round(ach / MFMA_PEAK_TFLOPS, 4),
+                              "traffic": read_traffic("fwd_kernel", p.w.name),
+                              "kernel": "fwd_kernel", "workload": p.w.name,
+                              "avg_launch_ms": round(t, 4), "flops_per_launch": p.flops,
+                              "dense_count_tflops": round(4 * p.w.B * p.w.H_q * p.w.S_q * p.w.S_k * p.w.D
+                                                          / (t * 1e-3) / 1e12, 2)}
+    if decode:
+        p, t = decode[0]
+        gbs = kv_bytes(p.w) / (t * 1e-3) / 1e9
+        dec = {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+               "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": read_traffic("decode_split_kernel", p.w.name),
+               "kernels": "decode_split_kernel + decode_merge_kernel", "workload": p.w.name,
+               "avg_call_us": round(t * 1e3, 2), "kv_bytes_per_call": kv_bytes(p.w)}
+        if prefill:
+            result["decode"] = dec
+        else:
+            result["roofline"] = dec
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(parts, args.cpu_budget)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,138 @@
+/*
+ * sa_attn.h — streaming exact attention (online softmax) for AMD MI355X (gfx950).
+ *
+ * C ABI of libsa_attn.so.  Every computing entry point is asynchronous on the
+ * caller's HIP stream; the library never allocates, frees or synchronises
+ * device memory and keeps no state between calls except a cached device
+ * property (compute-unit count) per device.
+ *
+ * What is computed.  For batch b, query head h (reading key/value head
+ * h / (H_q / H_kv): consecutive grouping of query heads over KV heads, as the
+ * "Attention API" page reshapes queries to (T, H_kv, G, D) in
+ * compute_hybrid_attention_store), query row i and key j:
+ *
+ *   s[i,j]   = scale * dot(q[b,i,h,:], k[b,j,hk,:]) - slope[h] * |i + S_k - S_q - j|
+ *   visible  = (!causal || j <= i + S_k - S_q) && (mask == NULL || mask[b,j] != 0)
+ *   lse[i]   = log(sum over visible j of exp(s[i,j]))            (natural log)
+ *   out[i,:] = sum over visible j of exp(s[i,j] - lse[i]) * v[b,j,hk,:]
+ *
+ * computed in one streaming sweep over key/value tiles with running float32
+ * row maximum and row sum ("StreamAttention: Fused Online Softmax Attention",
+ * section "Kernel Design (Fused Online Softmax)"; "Attention API" page,
+ * online_softmax_attention).  A row with no visible key yields out = 0 and
+ * lse = -inf, never NaN ("flash-attn-volta" page, section "Stability").
+ * Causal alignment is bottom-right (the last query row sees every key); with
+ * S_q == S_k it is the usual j <= i.
+ *
+ * Conventions shared by all entry points:
+ *  - Tensors are dense, row-major, with the shapes given per argument.
+ *  - q, k, v, out and the decode workspace must be 16-byte aligned; the mask
+ *    and slopes need only their natural alignment.
+ *  - Supported: D in {64, 128}; dtype SA_F16 or SA_BF16 (q, k, v and out all
+ *    of that type); 1 <= H_kv <= H_q with H_q % H_kv == 0.
+ *  - Inputs are read-only.  out and lse must not overlap any input.
+ *  - Return value: SA_OK or an sa_status code.  All arguments are validated
+ *    before anything is launched; on an error nothing is launched and the
+ *    outputs are untouched.  sa_last_error() then holds a description.
+ *    There is no fallback path: an unsupported request fails.
+ *  - Calls on one stream are ordered; calls on different streams that write
+ *    the same outputs or workspace race.
+ */
+#ifndef SA_ATTN_H
+#define SA_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  SA_OK = 0,
+  SA_ERR_INVALID_ARG = 1,  /* null/misaligned pointer, negative or inconsistent size */
+  SA_ERR_UNSUPPORTED = 2,  /* valid request outside what the kernels implement (D, dtype) */
+  SA_ERR_WORKSPACE = 3,    /* decode workspace missing or smaller than required */
+  SA_ERR_HIP = 4           /* a HIP runtime call or kernel launch failed */
+} sa_status;
+
+typedef enum { SA_F16 = 0, SA_BF16 = 1 } sa_dtype;
+
+/* hipStream_t without pulling HIP headers into C callers. */
+typedef struct ihipStream_t* sa_stream_t;
+
+/*
+ * Attention forward (prefill), the operation of the "StreamAttention" page's
+ * API Reference, forward(query, key, value, causal, return_lse,
+ * attention_mask, alibi_slopes), with a boolean key-padding mask as in its
+ * Quick Start, and the flash_attn_forward(..., return_softmax_lse) of the
+ * "flash-attn-volta" page, section "Use".
+ *
+ *   q     [B, S_q, H_q, D]   dtype, device
+ *   k, v  [B, S_k, H_kv, D]  dtype, device
+ *   out   [B, S_q, H_q, D]   dtype, device; every element is written
+ *   lse   [B, H_q, S_q]      float32, device, natural log; NULL = not written
+ *   scale  multiplies q.k in float32 (callers usually pass 1/sqrt(D))
+ *   causal 0 or 1 (bottom-right aligned, see above)
+ *   key_padding_mask [B, S_k] uint8 device, nonzero = keep; NULL = all keep
+ *   alibi_slopes     [H_q] float32 device; NULL = no bias
+ *
+ * B == 0 or S_q == 0 is a successful no-op.  S_k == 0 writes out = 0 and
+ * lse = -inf.  Errors: SA_ERR_INVALID_ARG, SA_ERR_UNSUPPORTED, SA_ERR_HIP.
+ */
+int sa_attn_fwd(const void* q, const void* k, const void* v, void* out, float* lse,
+                int B, int S_q, int S_k, int H_q, int H_kv, int D, float scale,
+                int causal, const uint8_t* key_padding_mask, const float* alibi_slopes,
+                int dtype, sa_stream_t stream);
+
+/*
+ * Bytes of device workspace sa_attn_decode needs for these sizes (an upper
+ * bound that holds for every H_kv dividing H_q).  Pure host arithmetic: no
+ * HIP call.  Returns 0 when a size is negative or the result would overflow.
+ */
+size_t sa_attn_decode_workspace_size(int B, int H_q, int S_k, int D);
+
+/*
+ * Single-token attention over a key/value cache (S_q = 1), split over the key
+ * axis: each split streams its keys once for all H_q / H_kv query heads that
+ * share a KV head and writes a normalised partial output and its log-sum-exp;
+ * a second kernel merges the splits with log-sum-exp weights ("StreamAttention"
+ * page, "Engine Direction": partial online-softmax states merged in a second
+ * kernel; "Distributed and Long-Context Variants": log-sum-exp weighted
+ * combining).  The result equals sa_attn_fwd with S_q = 1 (for which the
+ * bottom-right causal rule hides nothing).
+ *
+ *   q        [B, 1, H_q, D]    dtype, device
+ *   k_cache  [B, S_k, H_kv, D] dtype, device
+ *   v_cache  [B, S_k, H_kv, D] dtype, device
+ *   out      [B, 1, H_q, D]    dtype, device
+ *   lse      [B, H_q, 1]       float32, device; NULL = not written
+ *   key_padding_mask [B, S_k] uint8 (nonzero = keep) or NULL
+ *   alibi_slopes [H_q] float32 or NULL; the bias is -slope * (S_k - 1 - j)
+ *   workspace, workspace_bytes: caller-owned device scratch of at least
+ *     sa_attn_decode_workspace_size(B, H_q, S_k, D) bytes, 16-byte aligned;
+ *     its contents on entry do not matter and on return are unspecified.
+ *
+ * B == 0 is a no-op; S_k == 0 writes out = 0, lse = -inf.  Errors:
+ * SA_ERR_INVALID_ARG, SA_ERR_UNSUPPORTED, SA_ERR_WORKSPACE, SA_ERR_HIP.
+ */
+int sa_attn_decode(const void* q, const void* k_cache, const void* v_cache,
+                   void* out, float* lse, int B, int S_k, int H_q, int H_kv, int D,
+                   float scale, const uint8_t* key_padding_mask, const float* alibi_slopes,
+                   int dtype, void* workspace, size_t workspace_bytes, sa_stream_t stream);
+
+/* Number of key splits sa_attn_decode uses for these sizes on a device with
+ * num_cu compute units (host arithmetic only; exposed for tests and tools). */
+int sa_attn_decode_num_splits(int B, int S_k, int H_q, int H_kv, int num_cu);
+
+/* Static description of a status code. */
+const char* sa_status_string(int status);
+
+/* Description of the last non-OK return on the calling thread ("" if none). */
+const char* sa_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SA_ATTN_H */

@@ -1,0 +1,217 @@
+"""Streaming exact attention (online softmax) for AMD MI355X — Python binding.
+
+A thin ctypes layer over ``libsa_attn.so`` (C ABI declared in
+``include/sa_attn.h``).  It only marshals arguments: it checks tensor
+devices, dtypes, shapes and contiguity, passes raw device pointers and the
+current HIP stream, and raises on a non-OK status.  All arithmetic runs in the
+library's HIP kernels; there is no CPU or PyTorch fallback, and every call
+raises if the library was not built.
+
+Functions keep the names of the C entry points:
+
+* ``attn_fwd(q, k, v, causal=False, scale=None, key_padding_mask=None,
+  alibi_slopes=None, out=None, lse=None, return_lse=True)``
+* ``attn_decode(q, k_cache, v_cache, scale=None, key_padding_mask=None,
+  alibi_slopes=None, out=None, lse=None, workspace=None, return_lse=True)``
+* ``decode_workspace_size(B, H_q, S_k, D)`` and ``decode_num_splits(...)``
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+from pathlib import Path
+from typing import Optional
+
+import torch
+
+LIB_PATH = Path(__file__).resolve().parent / "libsa_attn.so"
+
+SA_OK, SA_ERR_INVALID_ARG, SA_ERR_UNSUPPORTED, SA_ERR_WORKSPACE, SA_ERR_HIP = range(5)
+SA_F16, SA_BF16 = 0, 1
+_DTYPE = {torch.float16: SA_F16, torch.bfloat16: SA_BF16}
+
+# Every symbol the public header declares, with its ctypes signature.
+_VP, _FP, _U8P = ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p
+_I, _F, _SZ = ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+SIGNATURES = {
+    "sa_attn_fwd": (_I, [_VP, _VP, _VP, _VP, _FP, _I, _I, _I, _I, _I, _I, _F, _I, _U8P, _FP, _I, _VP]),
+    "sa_attn_decode_workspace_size": (_SZ, [_I, _I, _I, _I]),
+    "sa_attn_decode": (_I, [_VP, _VP, _VP, _VP, _FP, _I, _I, _I, _I, _I, _F, _U8P, _FP, _I, _VP, _SZ, _VP]),
+    "sa_attn_decode_num_splits": (_I, [_I, _I, _I, _I, _I]),
+    "sa_status_string": (ctypes.c_char_p, [_I]),
+    "sa_last_error": (ctypes.c_char_p, []),
+}
+
+_lib: Optional[ctypes.CDLL] = None
+
+
+class SaAttnError(RuntimeError):
+    """A non-OK status from libsa_attn."""
+
+    def __init__(self, status: int, detail: str):
+        self.status = status
+        super().__init__(f"{status_string(status)}: {detail}")
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded library; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not LIB_PATH.exists():
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with `python -m online_softmax_amd.build` "
+                               "(there is no fallback implementation)")
+        h = ctypes.CDLL(str(LIB_PATH))
+        for name, (res, args) in SIGNATURES.items():
+            fn = getattr(h, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = h
+    return _lib
+
+
+def status_string(status: int) -> str:
+    return lib().sa_status_string(status).decode()
+
+
+def last_error() -> str:
+    return lib().sa_last_error().decode()
+
+
+def _check(status: int) -> None:
+    if status != SA_OK:
+        raise SaAttnError(status, last_error())
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(dev: torch.device) -> int:
+    return torch.cuda.current_stream(dev).cuda_stream
+
+
+def _need(t: torch.Tensor, name: str, dtype=None, shape=None, device=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on a GPU device (got {t.device})")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _mask_arg(mask, B, S_k, dev):
+    if mask is None:
+        return None
+    if mask.dtype == torch.bool:
+        mask = mask.view(torch.uint8)
+    _need(mask, "key_padding_mask", torch.uint8, (B, S_k), dev)
+    return mask
+
+
+def attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = False,
+             scale: Optional[float] = None, key_padding_mask: Optional[torch.Tensor] = None,
+             alibi_slopes: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
+             lse: Optional[torch.Tensor] = None, return_lse: bool = True):
+    """Attention forward through ``sa_attn_fwd``.
+
+    q ``[B, S_q, H_q, D]``, k/v ``[B, S_k, H_kv, D]`` (fp16 or bf16, same
+    device); key_padding_mask ``[B, S_k]`` bool/uint8 (nonzero keeps);
+    alibi_slopes float32 ``[H_q]``.  Returns ``out`` (and float32 ``lse``
+    ``[B, H_q, S_q]`` when ``return_lse``).
+    """
+    _need(q, "q")
+    if q.dtype not in _DTYPE:
+        raise ValueError(f"unsupported dtype {q.dtype}")
+    dev = q.device
+    B, S_q, H_q, D = q.shape
+    _need(k, "k", q.dtype, None, dev)
+    if k.dim() != 4 or k.shape[0] != B or k.shape[3] != D:
+        raise ValueError(f"k has shape {tuple(k.shape)}, incompatible with q {tuple(q.shape)}")
+    S_k, H_kv = k.shape[1], k.shape[2]
+    _need(v, "v", q.dtype, k.shape, dev)
+    mask = _mask_arg(key_padding_mask, B, S_k, dev)
+    if alibi_slopes is not None:
+        _need(alibi_slopes, "alibi_slopes", torch.float32, (H_q,), dev)
+    if out is None:
+        out = torch.empty_like(q)
+    _need(out, "out", q.dtype, q.shape, dev)
+    if lse is None and return_lse:
+        lse = torch.empty((B, H_q, S_q), dtype=torch.float32, device=dev)
+    if lse is not None:
+        _need(lse, "lse", torch.float32, (B, H_q, S_q), dev)
+    sc = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    st = lib().sa_attn_fwd(q.data_ptr(), _ptr(k), _ptr(v), out.data_ptr(), _ptr(lse),
+                           B, S_q, S_k, H_q, H_kv, D, sc, int(bool(causal)), _ptr(mask),
+                           _ptr(alibi_slopes), _DTYPE[q.dtype], _stream(dev))
+    _check(st)
+    return (out, lse) if return_lse else out
+
+
+def decode_workspace_size(B: int, H_q: int, S_k: int, D: int) -> int:
+    return int(lib().sa_attn_decode_workspace_size(B, H_q, S_k, D))
+
+
+def decode_num_splits(B: int, S_k: int, H_q: int, H_kv: int, num_cu: int) -> int:
+    return int(lib().sa_attn_decode_num_splits(B, S_k, H_q, H_kv, num_cu))
+
+
+def decode_workspace(B: int, H_q: int, S_k: int, D: int, device) -> torch.Tensor:
+    """A device byte buffer large enough for ``attn_decode`` at these sizes."""
+    n = decode_workspace_size(B, H_q, S_k, D)
+    return torch.empty(max(n, 16), dtype=torch.uint8, device=device)
+
+
+def attn_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                scale: Optional[float] = None, key_padding_mask: Optional[torch.Tensor] = None,
+                alibi_slopes: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
+                lse: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+                return_lse: bool = True):
+    """Single-token attention through ``sa_attn_decode`` (split-KV + merge).
+
+    q ``[B, 1, H_q, D]``; k_cache/v_cache ``[B, S_k, H_kv, D]``.  Returns
+    ``out [B, 1, H_q, D]`` (and float32 ``lse [B, H_q, 1]``).
+    """
+    _need(q, "q")
+    if q.dtype not in _DTYPE:
+        raise ValueError(f"unsupported dtype {q.dtype}")
+    dev = q.device
+    B, one, H_q, D = q.shape
+    if one != 1:
+        raise ValueError("decode takes exactly one query token per sequence")
+    _need(k_cache, "k_cache", q.dtype, None, dev)
+    if k_cache.dim() != 4 or k_cache.shape[0] != B or k_cache.shape[3] != D:
+        raise ValueError(f"k_cache has shape {tuple(k_cache.shape)}, incompatible with q")
+    S_k, H_kv = k_cache.shape[1], k_cache.shape[2]
+    _need(v_cache, "v_cache", q.dtype, k_cache.shape, dev)
+    mask = _mask_arg(key_padding_mask, B, S_k, dev)
+    if alibi_slopes is not None:
+        _need(alibi_slopes, "alibi_slopes", torch.float32, (H_q,), dev)
+    if out is None:
+        out = torch.empty_like(q)
+    _need(out, "out", q.dtype, q.shape, dev)
+    if lse is None and return_lse:
+        lse = torch.empty((B, H_q, 1), dtype=torch.float32, device=dev)
+    if lse is not None:
+        _need(lse, "lse", torch.float32, (B, H_q, 1), dev)
+    if workspace is None:
+        workspace = decode_workspace(B, H_q, S_k, D, dev)
+    _need(workspace, "workspace", None, None, dev)
+    sc = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    st = lib().sa_attn_decode(q.data_ptr(), _ptr(k_cache), _ptr(v_cache), out.data_ptr(), _ptr(lse),
+                              B, S_k, H_q, H_kv, D, sc, _ptr(mask), _ptr(alibi_slopes),
+                              _DTYPE[q.dtype], workspace.data_ptr(),
+                              workspace.numel() * workspace.element_size(), _stream(dev))
+    _check(st)
+    return (out, lse) if return_lse else out
+
+
+__all__ = ["attn_fwd", "attn_decode", "decode_workspace_size", "decode_num_splits",
+           "decode_workspace", "lib", "last_error", "status_string", "SaAttnError",
+           "SIGNATURES", "LIB_PATH", "SA_OK", "SA_ERR_INVALID_ARG", "SA_ERR_UNSUPPORTED",
+           "SA_ERR_WORKSPACE", "SA_ERR_HIP", "SA_F16", "SA_BF16"]

@@ -1,0 +1,70 @@
+// Device-side types and helpers shared by the attention kernels (gfx950).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace sa {
+
+constexpr float kLog2e = 1.4426950408889634f;  // log2(e): e^x = 2^(x log2 e)
+constexpr float kLn2 = 0.6931471805599453f;    // ln(2)
+constexpr float kNegInf = -__builtin_huge_valf();
+
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+
+// Element-type traits.  Storage is raw 16-bit words; these convert and feed
+// the 32x32x16 matrix-core instruction of the matching type.
+struct F16 {
+  __device__ static inline f32x16 mma(u32x4 a, u32x4 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
+                                                  __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+  }
+  // Two floats to a packed pair, round to nearest even.
+  __device__ static inline uint32_t pack2(float lo, float hi) {
+    f32x2 v = {lo, hi};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, f16x2));
+  }
+};
+
+struct BF16 {
+  __device__ static inline f32x16 mma(u32x4 a, u32x4 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+  }
+  __device__ static inline uint32_t pack2(float lo, float hi) {
+    f32x2 v = {lo, hi};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
+  }
+};
+
+__device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Value held by the lane 32 positions away (the other half of the wave).
+__device__ inline float swap_halves(float x) { return __shfl_xor(x, 32, 64); }
+
+// Transposing LDS read: in every group of 16 lanes, lane t supplies the
+// address of four consecutive 16-bit words; lane u receives word (u % 4) of
+// the chunks supplied by lanes u/4, 4 + u/4, 8 + u/4 and 12 + u/4.
+__device__ inline u32x2 lds_read_tr(const uint16_t* p) {
+  i16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p));
+  return __builtin_bit_cast(u32x2, r);
+}
+
+// Workgroups are dealt to the eight XCDs round-robin (id % 8).  Renumber them
+// so that each XCD receives one contiguous run of work items, keeping the
+// items that share key/value rows inside one XCD's L2.
+__device__ inline int xcd_contiguous(int id, int n) {
+  const int per = n >> 3, rem = n & 7, x = id & 7, slot = id >> 3;
+  return x < rem ? x * (per + 1) + slot : rem * (per + 1) + (x - rem) * per + slot;
+}
+
+}  // namespace sa

@@ -1,0 +1,179 @@
+// Host-side argument checking, decode split sizing and error reporting.
+#include "host_logic.hpp"
+
+#include <algorithm>
+#include <climits>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+
+#include "../../include/sa_attn.h"
+
+namespace sa {
+
+namespace {
+thread_local char g_err[512] = "";
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+// Byte ranges [a, a + na) and [b, b + nb) intersect.
+bool overlap(const void* a, size_t na, const void* b, size_t nb) {
+  if (!a || !b || na == 0 || nb == 0) return false;
+  uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+  return x < y + nb && y < x + na;
+}
+
+// Product of non-negative ints in int64 with an overflow guard.
+bool mul_ok(int64_t* acc, int64_t v) {
+  if (v < 0) return false;
+  if (v != 0 && *acc > INT64_C(0x3fffffffffffffff) / v) return false;
+  *acc *= v;
+  return true;
+}
+
+int check_common(int dtype, int D, int B, int S_k, int H_q, int H_kv, float scale) {
+  if (dtype != SA_F16 && dtype != SA_BF16)
+    return fail(SA_ERR_UNSUPPORTED, "dtype %d is not SA_F16 (0) or SA_BF16 (1)", dtype);
+  if (D != 64 && D != 128)
+    return fail(SA_ERR_UNSUPPORTED, "head dimension D=%d is not supported (64 or 128)", D);
+  if (B < 0 || S_k < 0)
+    return fail(SA_ERR_INVALID_ARG, "negative size (B=%d, S_k=%d)", B, S_k);
+  if (H_q < 1 || H_kv < 1)
+    return fail(SA_ERR_INVALID_ARG, "head counts must be positive (H_q=%d, H_kv=%d)", H_q, H_kv);
+  if (H_q % H_kv != 0)
+    return fail(SA_ERR_INVALID_ARG, "H_q=%d is not a multiple of H_kv=%d", H_q, H_kv);
+  if (!std::isfinite(scale))
+    return fail(SA_ERR_INVALID_ARG, "scale is not finite");
+  return SA_OK;
+}
+}  // namespace
+
+int fail(int status, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  std::vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return status;
+}
+
+void clear_error() { g_err[0] = '\0'; }
+const char* last_error() { return g_err; }
+
+const char* status_string(int status) {
+  switch (status) {
+    case SA_OK: return "SA_OK";
+    case SA_ERR_INVALID_ARG: return "SA_ERR_INVALID_ARG";
+    case SA_ERR_UNSUPPORTED: return "SA_ERR_UNSUPPORTED";
+    case SA_ERR_WORKSPACE: return "SA_ERR_WORKSPACE";
+    case SA_ERR_HIP: return "SA_ERR_HIP";
+    default: return "unknown sa_status";
+  }
+}
+
+int check_fwd(const FwdShape& s, bool* noop) {
+  *noop = false;
+  int st = check_common(s.dtype, s.D, s.B, s.S_k, s.H_q, s.H_kv, s.scale);
+  if (st != SA_OK) return st;
+  if (s.S_q < 0) return fail(SA_ERR_INVALID_ARG, "negative S_q=%d", s.S_q);
+  if (s.causal != 0 && s.causal != 1) return fail(SA_ERR_INVALID_ARG, "causal must be 0 or 1");
+  if (s.B == 0 || s.S_q == 0) { *noop = true; return SA_OK; }
+  int64_t nq = 1, nk = 1;
+  if (!mul_ok(&nq, s.B) || !mul_ok(&nq, s.S_q) || !mul_ok(&nq, s.H_q) || !mul_ok(&nq, s.D) ||
+      !mul_ok(&nk, s.B) || !mul_ok(&nk, s.S_k) || !mul_ok(&nk, s.H_kv) || !mul_ok(&nk, s.D))
+    return fail(SA_ERR_INVALID_ARG, "tensor sizes overflow");
+  // Workgroups: B * H_q * ceil(S_q / 128) must fit a 1-D grid.
+  int64_t items = (int64_t)s.B * s.H_q * ((s.S_q + 127) / 128);
+  if (items > INT32_MAX) return fail(SA_ERR_INVALID_ARG, "too many query blocks (%lld)", (long long)items);
+  if (!s.q || !s.out) return fail(SA_ERR_INVALID_ARG, "q and out must not be NULL");
+  if (s.S_k > 0 && (!s.k || !s.v)) return fail(SA_ERR_INVALID_ARG, "k and v must not be NULL when S_k > 0");
+  if (!aligned(s.q, 16) || !aligned(s.out, 16) || (s.k && !aligned(s.k, 16)) || (s.v && !aligned(s.v, 16)))
+    return fail(SA_ERR_INVALID_ARG, "q, k, v and out must be 16-byte aligned");
+  if (s.lse && !aligned(s.lse, 4)) return fail(SA_ERR_INVALID_ARG, "lse must be 4-byte aligned");
+  if (s.slopes && !aligned(s.slopes, 4)) return fail(SA_ERR_INVALID_ARG, "alibi_slopes must be 4-byte aligned");
+  const size_t qb = (size_t)nq * 2, kb = (size_t)nk * 2;
+  const size_t lb = (size_t)s.B * s.H_q * s.S_q * 4;
+  const size_t mb = (size_t)s.B * s.S_k, sb = (size_t)s.H_q * 4;
+  const void* ins[5] = {s.q, s.k, s.v, s.mask, s.slopes};
+  const size_t insz[5] = {qb, kb, kb, mb, sb};
+  for (int i = 0; i < 5; ++i) {
+    if (overlap(s.out, qb, ins[i], insz[i]) || overlap(s.lse, s.lse ? lb : 0, ins[i], insz[i]))
+      return fail(SA_ERR_INVALID_ARG, "out/lse overlap an input");
+  }
+  if (overlap(s.out, qb, s.lse, s.lse ? lb : 0)) return fail(SA_ERR_INVALID_ARG, "out and lse overlap");
+  return SA_OK;
+}
+
+int decode_num_splits(int B, int S_k, int H_q, int H_kv, int num_cu) {
+  if (B <= 0 || S_k <= 0 || H_q <= 0 || H_kv <= 0 || H_q % H_kv) return 1;
+  const int G = H_q / H_kv;
+  const int64_t groups = (int64_t)B * H_kv * ((G + kDecodeHeadGroup - 1) / kDecodeHeadGroup);
+  const int max_splits = (int)std::min<int64_t>(kDecodeMaxSplits, (S_k + kDecodeStepKeys - 1) / kDecodeStepKeys);
+  // Aim for two four-wave workgroups per compute unit so that each CU keeps
+  // eight waves of key/value loads in flight.
+  const int64_t target = 2 * (int64_t)(num_cu > 0 ? num_cu : 1);
+  int64_t splits = (target + groups - 1) / groups;
+  if (splits < 1) splits = 1;
+  if (splits > max_splits) splits = max_splits;
+  // Round to whole steps per split, then drop splits that would be empty.
+  const int chunk = decode_chunk(S_k, (int)splits);
+  return (S_k + chunk - 1) / chunk;
+}
+
+int decode_chunk(int S_k, int splits) {
+  if (splits < 1) splits = 1;
+  int per = (S_k + splits - 1) / splits;
+  int steps = (per + kDecodeStepKeys - 1) / kDecodeStepKeys;
+  if (steps < 1) steps = 1;
+  return steps * kDecodeStepKeys;
+}
+
+size_t decode_workspace_size(int B, int H_q, int S_k, int D) {
+  if (B < 0 || H_q < 0 || S_k < 0 || D < 0) return 0;
+  int64_t max_splits = std::min<int64_t>(kDecodeMaxSplits, (S_k + kDecodeStepKeys - 1) / kDecodeStepKeys);
+  if (max_splits < 1) max_splits = 1;
+  int64_t n = 1;
+  if (!mul_ok(&n, B) || !mul_ok(&n, H_q) || !mul_ok(&n, max_splits)) return 0;
+  int64_t floats = n;
+  if (!mul_ok(&floats, (int64_t)D + 1)) return 0;
+  // Partial outputs [B, H_q, splits, D] then partial lse [B, H_q, splits],
+  // the second region starting on a 256-byte boundary.
+  int64_t obytes = ((n * D * 4) + 255) / 256 * 256;
+  return (size_t)(obytes + n * 4);
+}
+
+int check_decode(const DecodeShape& s, bool* noop) {
+  *noop = false;
+  int st = check_common(s.dtype, s.D, s.B, s.S_k, s.H_q, s.H_kv, s.scale);
+  if (st != SA_OK) return st;
+  if (s.B == 0) { *noop = true; return SA_OK; }
+  int64_t nk = 1;
+  if (!mul_ok(&nk, s.B) || !mul_ok(&nk, s.S_k) || !mul_ok(&nk, s.H_kv) || !mul_ok(&nk, s.D))
+    return fail(SA_ERR_INVALID_ARG, "tensor sizes overflow");
+  if (!s.q || !s.out) return fail(SA_ERR_INVALID_ARG, "q and out must not be NULL");
+  if (s.S_k > 0 && (!s.k || !s.v)) return fail(SA_ERR_INVALID_ARG, "k_cache and v_cache must not be NULL when S_k > 0");
+  if (!aligned(s.q, 16) || !aligned(s.out, 16) || (s.k && !aligned(s.k, 16)) || (s.v && !aligned(s.v, 16)))
+    return fail(SA_ERR_INVALID_ARG, "q, k_cache, v_cache and out must be 16-byte aligned");
+  if (s.lse && !aligned(s.lse, 4)) return fail(SA_ERR_INVALID_ARG, "lse must be 4-byte aligned");
+  if (s.slopes && !aligned(s.slopes, 4)) return fail(SA_ERR_INVALID_ARG, "alibi_slopes must be 4-byte aligned");
+  const size_t need = decode_workspace_size(s.B, s.H_q, s.S_k, s.D);
+  if (need == 0) return fail(SA_ERR_INVALID_ARG, "tensor sizes overflow");
+  if (!s.workspace) return fail(SA_ERR_WORKSPACE, "workspace is NULL (%zu bytes needed)", need);
+  if (!aligned(s.workspace, 16)) return fail(SA_ERR_WORKSPACE, "workspace must be 16-byte aligned");
+  if (s.workspace_bytes < need)
+    return fail(SA_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed", s.workspace_bytes, need);
+  const size_t qb = (size_t)s.B * s.H_q * s.D * 2, kb = (size_t)nk * 2;
+  const size_t lb = (size_t)s.B * s.H_q * 4;
+  const void* ins[5] = {s.q, s.k, s.v, s.mask, s.slopes};
+  const size_t insz[5] = {qb, kb, kb, (size_t)s.B * s.S_k, (size_t)s.H_q * 4};
+  for (int i = 0; i < 5; ++i) {
+    if (overlap(s.out, qb, ins[i], insz[i]) || overlap(s.lse, s.lse ? lb : 0, ins[i], insz[i]) ||
+        overlap(s.workspace, need, ins[i], insz[i]))
+      return fail(SA_ERR_INVALID_ARG, "out, lse or workspace overlap an input");
+  }
+  if (overlap(s.out, qb, s.lse, s.lse ? lb : 0) || overlap(s.workspace, need, s.out, qb) ||
+      overlap(s.workspace, need, s.lse, s.lse ? lb : 0))
+    return fail(SA_ERR_INVALID_ARG, "out, lse and workspace overlap each other");
+  return SA_OK;
+}
+
+}  // namespace sa

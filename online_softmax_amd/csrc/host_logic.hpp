@@ -1,0 +1,47 @@
+// Host-side argument checking, decode split sizing and error reporting for
+// libsa_attn.  Plain C++: no HIP call is made here, so every function can run
+// (and is tested) on a machine without a GPU.
+#pragma once
+#include <cstddef>
+#include <cstdint>
+
+namespace sa {
+
+struct FwdShape {
+  const void* q; const void* k; const void* v; const void* out; const float* lse;
+  int B, S_q, S_k, H_q, H_kv, D; float scale; int causal;
+  const uint8_t* mask; const float* slopes; int dtype;
+};
+
+struct DecodeShape {
+  const void* q; const void* k; const void* v; const void* out; const float* lse;
+  int B, S_k, H_q, H_kv, D; float scale;
+  const uint8_t* mask; const float* slopes; int dtype;
+  const void* workspace; size_t workspace_bytes;
+};
+
+// Keys one decode split covers at least, and most splits per (batch, KV head,
+// query-head group).  A split is one workgroup of four waves.
+constexpr int kDecodeStepKeys = 128;
+constexpr int kDecodeMaxSplits = 256;
+// Query heads one decode workgroup serves at once (the MFMA column count).
+constexpr int kDecodeHeadGroup = 32;
+
+// Records a formatted message as the calling thread's last error and returns
+// the status unchanged.
+int fail(int status, const char* fmt, ...);
+void clear_error();
+const char* last_error();
+const char* status_string(int status);
+
+// Returns SA_OK, or an error status after recording the reason.  *noop is set
+// when the call is valid but has nothing to compute.
+int check_fwd(const FwdShape& s, bool* noop);
+int check_decode(const DecodeShape& s, bool* noop);
+
+int decode_num_splits(int B, int S_k, int H_q, int H_kv, int num_cu);
+// Keys per split for a split count (a multiple of kDecodeStepKeys).
+int decode_chunk(int S_k, int splits);
+size_t decode_workspace_size(int B, int H_q, int S_k, int D);
+
+}  // namespace sa

@@ -1,0 +1,191 @@
+// libsa_attn: C ABI entry points, kernel selection and launches.
+//
+// Everything here is host code around the kernels of prefill.hpp and
+// decode.hpp: validate (host_logic.cpp, no HIP call), pick the template
+// instance for {dtype, D, causal, mask, ALiBi}, launch on the caller's stream.
+#include <hip/hip_runtime.h>
+
+#include <mutex>
+
+#include "../../include/sa_attn.h"
+#include "decode.hpp"
+#include "host_logic.hpp"
+#include "prefill.hpp"
+
+namespace sa {
+namespace {
+
+constexpr int kMaxDevices = 64;
+
+// Compute-unit count per device, queried once.
+int num_cus(int* out) {
+  static std::once_flag flags[kMaxDevices];
+  static int cus[kMaxDevices];
+  static hipError_t errs[kMaxDevices];
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(SA_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices) return fail(SA_ERR_HIP, "device index %d out of range", dev);
+  std::call_once(flags[dev], [dev] {
+    errs[dev] = hipDeviceGetAttribute(&cus[dev], hipDeviceAttributeMultiprocessorCount, dev);
+  });
+  if (errs[dev] != hipSuccess)
+    return fail(SA_ERR_HIP, "hipDeviceGetAttribute: %s", hipGetErrorString(errs[dev]));
+  *out = cus[dev];
+  return SA_OK;
+}
+
+int launched(const char* what) {
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(SA_ERR_HIP, "%s launch failed: %s", what, hipGetErrorString(e));
+  return SA_OK;
+}
+
+template <class T, int D, bool C, bool M, bool A>
+void launch_fwd(const FwdArgs& args, hipStream_t st) {
+  hipLaunchKernelGGL((fwd_kernel<T, D, C, M, A>), dim3(args.nitems), dim3(256), 0, st, args);
+}
+
+template <class T, int D>
+void dispatch_fwd(const FwdArgs& args, bool causal, bool mask, bool alibi, hipStream_t st) {
+  const int key = (causal ? 4 : 0) | (mask ? 2 : 0) | (alibi ? 1 : 0);
+  switch (key) {
+    case 0: launch_fwd<T, D, false, false, false>(args, st); break;
+    case 1: launch_fwd<T, D, false, false, true>(args, st); break;
+    case 2: launch_fwd<T, D, false, true, false>(args, st); break;
+    case 3: launch_fwd<T, D, false, true, true>(args, st); break;
+    case 4: launch_fwd<T, D, true, false, false>(args, st); break;
+    case 5: launch_fwd<T, D, true, false, true>(args, st); break;
+    case 6: launch_fwd<T, D, true, true, false>(args, st); break;
+    default: launch_fwd<T, D, true, true, true>(args, st); break;
+  }
+}
+
+template <class T, int D, bool M, bool A>
+void launch_decode(const DecArgs& args, const MergeArgs& margs, int nwg, int nbh, hipStream_t st) {
+  hipLaunchKernelGGL((decode_split_kernel<T, D, M, A>), dim3(nwg), dim3(256), 0, st, args);
+  hipLaunchKernelGGL((decode_merge_kernel<T, D>), dim3(nbh), dim3(D), 0, st, margs);
+}
+
+template <class T, int D>
+void dispatch_decode(const DecArgs& args, const MergeArgs& margs, int nwg, int nbh, bool mask,
+                     bool alibi, hipStream_t st) {
+  const int key = (mask ? 2 : 0) | (alibi ? 1 : 0);
+  switch (key) {
+    case 0: launch_decode<T, D, false, false>(args, margs, nwg, nbh, st); break;
+    case 1: launch_decode<T, D, false, true>(args, margs, nwg, nbh, st); break;
+    case 2: launch_decode<T, D, true, false>(args, margs, nwg, nbh, st); break;
+    default: launch_decode<T, D, true, true>(args, margs, nwg, nbh, st); break;
+  }
+}
+
+}  // namespace
+}  // namespace sa
+
+extern "C" {
+
+int sa_attn_fwd(const void* q, const void* k, const void* v, void* out, float* lse, int B, int S_q,
+                int S_k, int H_q, int H_kv, int D, float scale, int causal,
+                const uint8_t* key_padding_mask, const float* alibi_slopes, int dtype,
+                sa_stream_t stream) {
+  using namespace sa;
+  clear_error();
+  FwdShape shp{q, k, v, out, lse, B, S_q, S_k, H_q, H_kv, D, scale, causal,
+               key_padding_mask, alibi_slopes, dtype};
+  bool noop = false;
+  int st = check_fwd(shp, &noop);
+  if (st != SA_OK || noop) return st;
+
+  FwdArgs args;
+  args.q = (const uint16_t*)q;
+  args.k = (const uint16_t*)k;
+  args.v = (const uint16_t*)v;
+  args.out = (uint16_t*)out;
+  args.lse = lse;
+  args.mask = key_padding_mask;
+  args.slopes = alibi_slopes;
+  args.B = B; args.S_q = S_q; args.S_k = S_k; args.H_q = H_q; args.H_kv = H_kv;
+  args.G = H_q / H_kv;
+  args.scale2 = scale * kLog2e;
+  args.nmb = (S_q + 127) / 128;
+  args.nitems = B * H_q * args.nmb;
+  const bool c = causal != 0, m = key_padding_mask != nullptr, al = alibi_slopes != nullptr;
+  hipStream_t hs = (hipStream_t)stream;
+  if (dtype == SA_F16) {
+    if (D == 64) dispatch_fwd<F16, 64>(args, c, m, al, hs);
+    else dispatch_fwd<F16, 128>(args, c, m, al, hs);
+  } else {
+    if (D == 64) dispatch_fwd<BF16, 64>(args, c, m, al, hs);
+    else dispatch_fwd<BF16, 128>(args, c, m, al, hs);
+  }
+  return launched("attention forward");
+}
+
+size_t sa_attn_decode_workspace_size(int B, int H_q, int S_k, int D) {
+  return sa::decode_workspace_size(B, H_q, S_k, D);
+}
+
+int sa_attn_decode_num_splits(int B, int S_k, int H_q, int H_kv, int num_cu) {
+  return sa::decode_num_splits(B, S_k, H_q, H_kv, num_cu);
+}
+
+int sa_attn_decode(const void* q, const void* k_cache, const void* v_cache, void* out, float* lse,
+                   int B, int S_k, int H_q, int H_kv, int D, float scale,
+                   const uint8_t* key_padding_mask, const float* alibi_slopes, int dtype,
+                   void* workspace, size_t workspace_bytes, sa_stream_t stream) {
+  using namespace sa;
+  clear_error();
+  DecodeShape shp{q, k_cache, v_cache, out, lse, B, S_k, H_q, H_kv, D, scale,
+                  key_padding_mask, alibi_slopes, dtype, workspace, workspace_bytes};
+  bool noop = false;
+  int st = check_decode(shp, &noop);
+  if (st != SA_OK || noop) return st;
+  int cus = 0;
+  st = num_cus(&cus);
+  if (st != SA_OK) return st;
+
+  const int G = H_q / H_kv;
+  const int n_hg = (G + kDecodeHeadGroup - 1) / kDecodeHeadGroup;
+  const int splits = decode_num_splits(B, S_k, H_q, H_kv, cus);
+  const int chunk = decode_chunk(S_k, splits);
+  const int64_t nwg = (int64_t)B * H_kv * n_hg * splits;
+  if (nwg > INT32_MAX) return fail(SA_ERR_INVALID_ARG, "too many decode workgroups");
+
+  const size_t n = (size_t)B * H_q * splits;
+  DecArgs args;
+  args.q = (const uint16_t*)q;
+  args.k = (const uint16_t*)k_cache;
+  args.v = (const uint16_t*)v_cache;
+  args.mask = key_padding_mask;
+  args.slopes = alibi_slopes;
+  args.ws_o = (float*)workspace;
+  args.ws_lse = (float*)((char*)workspace + (n * D * 4 + 255) / 256 * 256);
+  args.B = B; args.S_k = S_k; args.H_q = H_q; args.H_kv = H_kv; args.G = G;
+  args.n_hg = n_hg; args.splits = splits; args.chunk = chunk;
+  args.scale2 = scale * kLog2e;
+
+  MergeArgs margs;
+  margs.ws_o = args.ws_o;
+  margs.ws_lse = args.ws_lse;
+  margs.out = (uint16_t*)out;
+  margs.lse = lse;
+  margs.splits = splits;
+
+  const bool m = key_padding_mask != nullptr, al = alibi_slopes != nullptr;
+  const int nbh = B * H_q;
+  hipStream_t hs = (hipStream_t)stream;
+  if (dtype == SA_F16) {
+    if (D == 64) dispatch_decode<F16, 64>(args, margs, (int)nwg, nbh, m, al, hs);
+    else dispatch_decode<F16, 128>(args, margs, (int)nwg, nbh, m, al, hs);
+  } else {
+    if (D == 64) dispatch_decode<BF16, 64>(args, margs, (int)nwg, nbh, m, al, hs);
+    else dispatch_decode<BF16, 128>(args, margs, (int)nwg, nbh, m, al, hs);
+  }
+  return launched("decode");
+}
+
+const char* sa_status_string(int status) { return sa::status_string(status); }
+
+const char* sa_last_error(void) { return sa::last_error(); }
+
+}  // extern "C"

@@ -1,0 +1,99 @@
+"""GPU parity of the split-KV decode path (sa_attn_decode) against the oracle.
+
+The oracle for one query token is the same definition as for prefill with
+S_q = 1 (the bottom-right causal rule hides nothing from the last row).
+"""
+import numpy as np
+import pytest
+import torch
+
+import online_softmax_amd as sa
+from parity import assert_lse_close, assert_out_close, oracle_for, to_dev
+from workloads import WORKLOADS, Workload, make_inputs, to_f64
+
+pytestmark = pytest.mark.gpu
+
+
+def run_decode(inp):
+    q, k, v, m, s = to_dev(inp)
+    out, lse = sa.attn_decode(q, k, v, scale=inp.w.scale, key_padding_mask=m, alibi_slopes=s)
+    torch.cuda.synchronize()
+    return to_f64(out.cpu()), lse.cpu().double().numpy()
+
+
+def check(inp, what=""):
+    w = inp.w
+    print(f"[decode] {what or w.name} B={w.B} S_k={w.S_k} H={w.H_q}/{w.H_kv} D={w.D} {w.dtype} "
+          f"mask={inp.mask is not None} alibi={inp.slopes is not None}", flush=True)
+    out, lse = run_decode(inp)
+    ref_o, ref_l = oracle_for(inp, causal=False)
+    dt = torch.float16 if w.dtype == "fp16" else torch.bfloat16
+    assert_out_close(out, ref_o, dt, what or w.name)
+    assert_lse_close(lse, ref_l, what or w.name)
+    return out, lse
+
+
+CASES = [
+    Workload("dec_k1", 2, 1, 1, 4, 4, 64, "fp16", seed=40),
+    Workload("dec_k100_g7", 3, 1, 100, 14, 2, 64, "fp16", seed=41),
+    Workload("dec_k1000_g8_mask", 2, 1, 1000, 16, 2, 128, "bf16", random_tail=400, seed=42),
+    Workload("dec_k5000_alibi", 2, 1, 5000, 8, 8, 64, "fp16", alibi=True, seed=43),
+    Workload("dec_k777_all", 2, 1, 777, 28, 4, 128, "bf16", alibi=True, random_tail=300, seed=44),
+    Workload("dec_g40_two_groups", 1, 1, 300, 40, 1, 64, "fp16", seed=45),
+    Workload("dec_k129_mha", 4, 1, 129, 6, 6, 128, "fp16", seed=46),
+]
+
+
+@pytest.mark.parametrize("w", CASES, ids=lambda w: w.name)
+def test_decode_cases(w):
+    check(make_inputs(w))
+
+
+def test_config4_full():
+    check(make_inputs(WORKLOADS["c4_decode_32k"]))
+
+
+def test_decode_empty_cache():
+    q = torch.randn(2, 1, 4, 64, device="cuda").half()
+    k = torch.zeros(2, 0, 2, 64, device="cuda").half()
+    out, lse = sa.attn_decode(q, k, k.clone())
+    torch.cuda.synchronize()
+    assert (out.float() == 0).all() and torch.isneginf(lse).all()
+
+
+def test_decode_fully_masked_row():
+    w = Workload("dec_masked", 2, 1, 500, 4, 2, 64, "fp16", seed=47)
+    inp = make_inputs(w)
+    inp.mask = torch.ones((2, 500), dtype=torch.uint8)
+    inp.mask[0] = 0
+    out, lse = check(inp, "fully masked batch row")
+    assert (out[0] == 0).all() and np.isneginf(lse[0]).all()
+
+
+def test_decode_matches_prefill_last_row():
+    """Decode of the last query equals row S-1 of a causal prefill on the same K/V."""
+    S = 700
+    w = Workload("dec_vs_fwd", 2, S, S, 8, 2, 64, "fp16", causal=True, alibi=True, seed=48)
+    inp = make_inputs(w)
+    q, k, v, m, s = to_dev(inp)
+    out_f, lse_f = sa.attn_fwd(q, k, v, causal=True, scale=w.scale, alibi_slopes=s)
+    out_d, lse_d = sa.attn_decode(q[:, S - 1:S].contiguous(), k, v, scale=w.scale, alibi_slopes=s)
+    torch.cuda.synchronize()
+    a, b = out_f[:, S - 1:S].double().cpu().numpy(), out_d.double().cpu().numpy()
+    assert np.abs(a - b).max() <= 2e-3
+    assert np.abs(lse_f[:, :, S - 1:S].cpu().numpy() - lse_d.cpu().numpy()).max() <= 1e-4
+
+
+def test_decode_workspace_errors():
+    w = Workload("dec_ws", 1, 1, 300, 4, 4, 64, "fp16", seed=49)
+    q, k, v, _, _ = to_dev(make_inputs(w))
+    small = torch.empty(16, dtype=torch.uint8, device="cuda")
+    with pytest.raises(sa.SaAttnError) as e:
+        sa.attn_decode(q, k, v, workspace=small)
+    assert e.value.status == sa.SA_ERR_WORKSPACE
+
+
+def test_decode_deterministic():
+    inp = make_inputs(Workload("dec_det", 2, 1, 3000, 14, 2, 64, "fp16", random_tail=100, seed=50))
+    a, b = run_decode(inp), run_decode(inp)
+    assert (a[0] == b[0]).all() and (a[1] == b[1]).all()

@@ -1,0 +1,185 @@
+"""GPU parity of the prefill kernel (sa_attn_fwd) against the float64 oracle.
+
+Every case draws seeded inputs from ``workloads``, runs the HIP kernel through
+the C ABI (via the ctypes binding) and compares element by element with
+``oracle.attention`` on the same values: outputs within 5e-3 + half an ulp of
+the output dtype, lse within 1e-3 (see tests/parity.py).
+"""
+import numpy as np
+import pytest
+import torch
+
+import online_softmax_amd as sa
+from parity import assert_lse_close, assert_out_close, oracle_for, to_dev
+from workloads import WORKLOADS, Workload, make_inputs, to_f64
+
+pytestmark = pytest.mark.gpu
+
+
+def run_fwd(inp, causal=None):
+    q, k, v, m, s = to_dev(inp)
+    w = inp.w
+    out, lse = sa.attn_fwd(q, k, v, causal=w.causal if causal is None else causal, scale=w.scale,
+                           key_padding_mask=m, alibi_slopes=s)
+    torch.cuda.synchronize()
+    return to_f64(out.cpu()), lse.cpu().double().numpy()
+
+
+def check(inp, rows=None, what=""):
+    print(f"[fwd] {what or inp.w.name} B={inp.w.B} S_q={inp.w.S_q} S_k={inp.w.S_k} "
+          f"H={inp.w.H_q}/{inp.w.H_kv} D={inp.w.D} {inp.w.dtype} causal={inp.w.causal} "
+          f"mask={inp.mask is not None} alibi={inp.slopes is not None}", flush=True)
+    out, lse = run_fwd(inp)
+    ref_o, ref_l = oracle_for(inp, rows=rows)
+    if rows is not None:
+        out, lse = out[:, rows], lse[:, :, rows]
+    dt = torch.float16 if inp.w.dtype == "fp16" else torch.bfloat16
+    assert_out_close(out, ref_o, dt, what)
+    assert_lse_close(lse, ref_l, what)
+    return out, lse
+
+
+# Shapes span several 128-row query blocks and 64-key tiles with ragged tails.
+SMALL = []
+for D in (64, 128):
+    for dt in ("fp16", "bf16"):
+        for causal in (False, True):
+            SMALL.append(Workload(f"s200_D{D}_{dt}_c{int(causal)}", 2, 200, 200, 3, 3, D, dt,
+                                  causal=causal, seed=100 + D + causal))
+
+
+@pytest.mark.parametrize("w", SMALL, ids=lambda w: w.name)
+def test_small_plain(w):
+    check(make_inputs(w))
+
+
+FEATURES = [
+    Workload("mask_noncausal", 2, 150, 333, 4, 4, 64, "fp16", random_tail=200, seed=11),
+    Workload("mask_causal", 2, 333, 333, 4, 4, 128, "bf16", causal=True, random_tail=100, seed=12),
+    Workload("alibi_noncausal", 1, 190, 190, 8, 8, 64, "fp16", alibi=True, seed=13),
+    Workload("alibi_causal", 1, 260, 260, 8, 8, 128, "bf16", causal=True, alibi=True, seed=14),
+    Workload("all_features", 2, 300, 300, 8, 8, 128, "bf16", causal=True, alibi=True, random_tail=64, seed=15),
+    Workload("gqa_4to1", 2, 140, 140, 8, 2, 64, "fp16", causal=True, seed=16),
+    Workload("gqa_7to1_alibi", 1, 129, 129, 14, 2, 128, "fp16", alibi=True, seed=17),
+    Workload("sq_lt_sk_causal", 1, 77, 300, 4, 4, 64, "fp16", causal=True, seed=18),
+    Workload("sq_gt_sk_causal", 1, 300, 77, 4, 4, 64, "fp16", causal=True, seed=19),
+    Workload("sq_lt_sk_alibi", 1, 50, 200, 4, 4, 128, "bf16", causal=True, alibi=True, seed=20),
+    Workload("s1", 3, 1, 1, 2, 2, 64, "fp16", seed=21),
+    Workload("s7", 2, 7, 7, 2, 1, 64, "fp16", causal=True, seed=22),
+    Workload("s65", 1, 65, 65, 2, 2, 128, "fp16", causal=True, seed=23),
+    Workload("s1000", 1, 1000, 1000, 2, 2, 64, "bf16", causal=True, random_tail=300, seed=24),
+    Workload("q1_long", 2, 1, 1000, 4, 4, 64, "fp16", seed=25),
+]
+
+
+@pytest.mark.parametrize("w", FEATURES, ids=lambda w: w.name)
+def test_features(w):
+    check(make_inputs(w))
+
+
+def test_config1_full():
+    check(make_inputs(WORKLOADS["c1_fwd_256"]))
+
+
+def test_config2_full():
+    check(make_inputs(WORKLOADS["c2_causal_pad16"]))
+
+
+def _sample_rows(S, n, seed):
+    """Rows at the edges of tiles and blocks plus seeded random ones."""
+    base = {0, 1, 63, 64, 127, 128, S // 2, S - 129, S - 128, S - 65, S - 64, S - 2, S - 1}
+    rng = np.random.default_rng(seed)
+    base |= set(rng.integers(0, S, n).tolist())
+    return np.array(sorted(r for r in base if 0 <= r < S))
+
+
+@pytest.mark.parametrize("name", ["c3_causal_4096", "c3_noncausal_4096"])
+def test_config3_sampled(name):
+    w = WORKLOADS[name]
+    check(make_inputs(w), rows=_sample_rows(w.S_q, 24, 3), what=name)
+
+
+def test_config5_sampled():
+    w = WORKLOADS["c5_alibi_8192"]
+    inp = make_inputs(w)
+    assert inp.tails == [347, 289]
+    check(inp, rows=_sample_rows(w.S_q, 16, 5), what=w.name)
+
+
+def test_empty_keys():
+    """S_k = 0: out = 0 and lse = -inf."""
+    q = torch.randn(2, 10, 4, 64, device="cuda").half()
+    k = torch.zeros(2, 0, 4, 64, device="cuda").half()
+    out, lse = sa.attn_fwd(q, k, k.clone(), causal=False)
+    torch.cuda.synchronize()
+    assert (out.float() == 0).all() and torch.isneginf(lse).all()
+
+
+def test_noop_shapes():
+    q = torch.zeros(0, 5, 2, 64, device="cuda").half()
+    out, lse = sa.attn_fwd(q, q.clone(), q.clone())
+    assert out.shape == q.shape and lse.numel() == 0
+
+
+def test_fully_masked_rows():
+    """A batch row whose mask hides every key, and causal rows before the first key."""
+    w = Workload("masked_rows", 2, 130, 130, 2, 2, 64, "fp16", causal=True, seed=31)
+    inp = make_inputs(w)
+    inp.mask = torch.ones((2, 130), dtype=torch.uint8)
+    inp.mask[1, :] = 0
+    out, lse = check(inp, what="fully masked batch row")
+    assert (out[1] == 0).all() and np.isneginf(lse[1]).all()
+    # S_q > S_k with causal alignment at the bottom right: early rows see no key.
+    w2 = Workload("early_rows", 1, 200, 50, 2, 2, 64, "fp16", causal=True, seed=32)
+    out2, lse2 = check(make_inputs(w2), what="rows before the first key")
+    assert (out2[0, :150] == 0).all() and np.isneginf(lse2[0, :, :150]).all()
+
+
+def test_single_key_bitwise():
+    """S_k = 1: P = 1 exactly, so out equals v bit for bit."""
+    w = Workload("one_key", 2, 100, 1, 4, 2, 128, "bf16", seed=33)
+    inp = make_inputs(w)
+    out, lse = check(inp)
+    v = to_f64(inp.v)
+    for h in range(4):
+        assert (out[:, :, h, :] == v[:, 0:1, h // 2, :]).all()
+
+
+def test_overflow_guard():
+    """q.k far past the fp16 range stays finite with float32 scores."""
+    w = Workload("big_values", 1, 100, 100, 2, 2, 64, "fp16", causal=True, seed=34)
+    inp = make_inputs(w, scale_values=64.0)
+    check(inp, what="large magnitudes")
+
+
+def test_deterministic():
+    """Two runs of the same call are bitwise identical."""
+    inp = make_inputs(Workload("det", 2, 300, 300, 4, 4, 128, "bf16", causal=True, alibi=True,
+                               random_tail=50, seed=35))
+    a = run_fwd(inp)
+    b = run_fwd(inp)
+    assert (a[0] == b[0]).all() and (a[1] == b[1]).all()
+
+
+def test_causal_leak_bitwise():
+    """Changing keys/values no row may see leaves out and lse bit-identical."""
+    w = Workload("leak", 1, 256, 256, 4, 4, 64, "fp16", causal=True, pad_tail=40, seed=36)
+    inp = make_inputs(w)
+    a = run_fwd(inp)
+    g = torch.Generator().manual_seed(99)
+    k2, v2 = inp.k.clone(), inp.v.clone()
+    # Perturb the padded keys (hidden from every row).
+    k2[:, -40:] = torch.randn(k2[:, -40:].shape, generator=g).half()
+    v2[:, -40:] = torch.randn(v2[:, -40:].shape, generator=g).half()
+    inp2 = make_inputs(w)
+    inp2.k, inp2.v = k2, v2
+    b = run_fwd(inp2)
+    assert (a[0] == b[0]).all() and (a[1] == b[1]).all()
+    # Perturb keys after position 100: rows 0..100 must not change.
+    k3, v3 = inp.k.clone(), inp.v.clone()
+    k3[:, 101:] = torch.randn(k3[:, 101:].shape, generator=g).half()
+    v3[:, 101:] = torch.randn(v3[:, 101:].shape, generator=g).half()
+    inp3 = make_inputs(w)
+    inp3.k, inp3.v = k3, v3
+    c = run_fwd(inp3)
+    assert (a[0][:, :101] == c[0][:, :101]).all() and (a[1][:, :, :101] == c[1][:, :, :101]).all()
