@@ -3,6 +3,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace sa {
 
 constexpr float kLog2e = 1.4426950408889634f;  // log2(e): e^x = 2^(x log2 e)
@@ -48,8 +50,20 @@ struct BF16 {
 
 __device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
-// Value held by the lane 32 positions away (the other half of the wave).
-__device__ inline float swap_halves(float x) { return __shfl_xor(x, 32, 64); }
+// Combine x with the value the lane 32 positions away holds (the other half
+// of the wave), using v_permlane32_swap: with both operands x it returns the
+// low-half values in one result and the high-half values in the other.
+__device__ inline float max_halves(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ inline float sum_halves(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// True in every lane when the predicate holds in any lane of the wave.
+__device__ inline bool wave_any(bool p) { return __builtin_amdgcn_ballot_w64(p) != 0; }
 
 // Transposing LDS read: in every group of 16 lanes, lane t supplies the
 // address of four consecutive 16-bit words; lane u receives word (u % 4) of
@@ -58,6 +72,21 @@ __device__ inline u32x2 lds_read_tr(const uint16_t* p) {
   i16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p));
   return __builtin_bit_cast(u32x2, r);
 }
+
+// Buffer resource over [base, base + bytes): loads beyond the end read zero.
+__device__ inline __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, 0x00020000);
+}
+
+// Direct global-to-LDS copy of 16 bytes per lane: lane l's bytes land at
+// lds + 16 l (lds must be the same for the whole wave).
+__device__ inline void load_lds16(__amdgpu_buffer_rsrc_t r, void* lds, uint32_t voffset) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16, voffset, 0, 0, 0);
+}
+
+// Wait for this wave's outstanding vector-memory operations, including
+// global-to-LDS copies (vmcnt(0); the other counters are left alone).
+__device__ inline void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0f70); }
 
 // Workgroups are dealt to the eight XCDs round-robin (id % 8).  Renumber them
 // so that each XCD receives one contiguous run of work items, keeping the

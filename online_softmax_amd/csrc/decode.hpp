@@ -19,7 +19,8 @@
 // query heads as the 32 MFMA columns (unused columns hold zero queries), then
 // O^T += V^T P^T with V read transposed from LDS.  K goes straight from global
 // memory into the A-operand registers (one key row per lane); V passes through
-// a wave-private LDS slot.
+// a wave-private LDS slot.  Each wave issues the loads of NSUB sub-tiles at
+// once before computing any of them, to keep many bytes in flight per CU.
 #pragma once
 #include "common.hpp"
 
@@ -38,18 +39,20 @@ struct DecArgs {
 };
 
 template <class T, int D, bool MASK, bool ALIBI>
-__global__ __launch_bounds__(256) void decode_split_kernel(DecArgs a) {
+__global__ __launch_bounds__(256, 2) void decode_split_kernel(DecArgs a) {
   constexpr int VSTR = D + 32;           // V row stride in LDS (16-bit words)
   constexpr int KK = D / 16;
   constexpr int DB = D / 32;
   constexpr int VCH = 32 * D / 8 / 64;   // 16-byte V chunks per lane per 32-key sub-tile
   constexpr int RCH = D / 8;
+  constexpr int NSUB = D == 64 ? 4 : 2;  // sub-tiles loaded together per wave
   constexpr int VBYTES = 4 * 32 * VSTR * 2;
   constexpr int MBYTES = 3 * (2 + D) * 32 * 4;
   constexpr int SBYTES = VBYTES > MBYTES ? VBYTES : MBYTES;
   __shared__ __attribute__((aligned(16))) unsigned char smem[SBYTES];
 
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int li = lane & 31, g = lane >> 5;
 
   const int s = blockIdx.x % a.splits;
@@ -64,58 +67,65 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecArgs a) {
 
   const int k0 = s * a.chunk;
   const int k1 = min(a.S_k, k0 + a.chunk);
-  const int nsteps = k1 > k0 ? (k1 - k0 + 127) / 128 : 0;
+  const int nsub_total = k1 > k0 ? (k1 - k0 + 31) / 32 : 0;   // 32-key sub-tiles in the split
+  const int nsteps = (nsub_total + 4 * NSUB - 1) / (4 * NSUB);
   const int ipos = a.S_k - 1;  // the query's position on the key axis
 
+  const uint32_t qflip = a.scale2 < 0.f ? 0x80008000u : 0u;
+  const float sc2 = __builtin_fabsf(a.scale2);
   u32x4 qreg[KK];
   {
     const uint16_t* qp = a.q + ((size_t)b * a.H_q + (hvalid ? h : 0)) * D + 8 * g;
 #pragma unroll
-    for (int kk = 0; kk < KK; ++kk)
+    for (int kk = 0; kk < KK; ++kk) {
       qreg[kk] = hvalid ? *(const u32x4*)(qp + 16 * kk) : (u32x4){0, 0, 0, 0};
+      qreg[kk] ^= qflip;
+    }
   }
 
   const size_t rs = (size_t)a.H_kv * D;
   const uint16_t* kb = a.k + ((size_t)b * a.S_k * a.H_kv + hk) * D;
   const uint16_t* vb = a.v + ((size_t)b * a.S_k * a.H_kv + hk) * D;
   uint16_t* Vw = (uint16_t*)smem + w * 32 * VSTR;
+  const uint8_t* mrow = MASK ? a.mask + (size_t)b * a.S_k : nullptr;
 
-  u32x4 kr[KK], vr[VCH], kn[KK], vn[VCH];
-  auto load = [&](int st, u32x4* kd, u32x4* vd) {
-    const int base = k0 + 128 * st + 32 * w;
-    {
-      const int j = base + li;
-      const bool ok = j < k1;
-      const uint16_t* kp = kb + (size_t)(ok ? j : 0) * rs + 8 * g;
-#pragma unroll
-      for (int kk = 0; kk < KK; ++kk) kd[kk] = ok ? *(const u32x4*)(kp + 16 * kk) : (u32x4){0, 0, 0, 0};
-    }
-#pragma unroll
-    for (int u = 0; u < VCH; ++u) {
-      const int c = lane + 64 * u, row = c / RCH, col = (c % RCH) * 8;
-      const int j = base + row;
-      const bool ok = j < k1;
-      vd[u] = ok ? *(const u32x4*)(vb + (size_t)(ok ? j : 0) * rs + col) : (u32x4){0, 0, 0, 0};
-    }
-  };
-
-  float m_run = kNegInf, l_run = 0.f;
+  float m_ref = kNegInf, l_run = 0.f;
   f32x16 o[DB];
 #pragma unroll
   for (int db = 0; db < DB; ++db) o[db] = (f32x16){};
   const float slope2 = (ALIBI && hvalid) ? a.slopes[h] * kLog2e : 0.f;
   const int tr_key = 4 * g + ((lane & 15) >> 2);
   const int tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
-  const uint8_t* mrow = MASK ? a.mask + (size_t)b * a.S_k : nullptr;
 
-  if (nsteps > 0) load(0, kr, vr);
   for (int st = 0; st < nsteps; ++st) {
-    if (st + 1 < nsteps) load(st + 1, kn, vn);
-    const int base = k0 + 128 * st + 32 * w;
-    if (base < k1) {  // wave-uniform
+    // Sub-tiles are dealt to the waves round-robin: sub-tile u = w + 4 (st NSUB + v).
+    u32x4 kr[NSUB][KK], vr[NSUB][VCH];
+#pragma unroll
+    for (int v = 0; v < NSUB; ++v) {
+      const int base = k0 + 32 * (w + 4 * (st * NSUB + v));
+      const int j = base + li;
+      const bool ok = j < k1;
+      const uint16_t* kp = kb + (size_t)(ok ? j : k0) * rs + 8 * g;
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk) {
+        kr[v][kk] = *(const u32x4*)(kp + 16 * kk);
+        if (!ok) kr[v][kk] = (u32x4){0, 0, 0, 0};
+      }
+#pragma unroll
+      for (int u = 0; u < VCH; ++u) {
+        const int c = lane + 64 * u, row = c / RCH, col = (c % RCH) * 8;
+        const bool okv = base + row < k1;
+        vr[v][u] = *(const u32x4*)(vb + (size_t)(okv ? base + row : k0) * rs + col);
+        if (!okv) vr[v][u] = (u32x4){0, 0, 0, 0};
+      }
+    }
+#pragma unroll
+    for (int v = 0; v < NSUB; ++v) {
+      const int base = k0 + 32 * (w + 4 * (st * NSUB + v));
+      if (base >= k1) break;  // wave-uniform
       f32x16 sc = (f32x16){};
 #pragma unroll
-      for (int kk = 0; kk < KK; ++kk) sc = T::mma(kr[kk], qreg[kk], sc);
+      for (int kk = 0; kk < KK; ++kk) sc = T::mma(kr[v][kk], qreg[kk], sc);
       // Stage this sub-tile's V rows in the wave's LDS slot.  LDS operations
       // of one wave complete in order; the waits and compiler barriers keep
       // the compiler from moving the reads of the previous sub-tile past
@@ -125,19 +135,19 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecArgs a) {
 #pragma unroll
       for (int u = 0; u < VCH; ++u) {
         const int c = lane + 64 * u, row = c / RCH, col = (c % RCH) * 8;
-        *(u32x4*)&Vw[row * VSTR + col] = vr[u];
+        *(u32x4*)&Vw[row * VSTR + col] = vr[v][u];
       }
       __builtin_amdgcn_s_waitcnt(0xc07f);
       __asm__ volatile("" ::: "memory");
 
       const bool need_mask = MASK || base + 32 > k1;
       const float rel0 = (float)(ipos - base - 4 * g);
-      float mx = kNegInf;
+      const float bb = -slope2 * rel0;
+      float tmax = kNegInf;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int kofs = 8 * (r >> 2) + (r & 3);
-        float x = sc[r] * a.scale2;
-        if (ALIBI) x = fmaf(-slope2, rel0 - (float)kofs, x);
+        float x = ALIBI ? fmaf(sc[r], sc2, fmaf(slope2, (float)kofs, bb)) : sc[r];
         if (need_mask) {
           const int kj = base + 4 * g + kofs;
           bool vis = kj < k1;
@@ -145,18 +155,20 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecArgs a) {
           x = vis ? x : kNegInf;
         }
         sc[r] = x;
-        mx = fmaxf(mx, x);
+        tmax = fmaxf(tmax, x);
       }
-      mx = fmaxf(mx, swap_halves(mx));
-      const float m_new = fmaxf(m_run, mx);
+      tmax = max_halves(tmax);
+      if (!ALIBI) tmax *= sc2;
+      const float m_new = fmaxf(m_ref, tmax);
       const float m_use = m_new == kNegInf ? 0.f : m_new;
-      const float alpha = fast_exp2(m_run - m_use);
-      m_run = m_new;
+      const float alpha = fast_exp2(m_ref - m_use);
+      m_ref = m_new;
       float psum = 0.f;
       uint32_t pk[8];
 #pragma unroll
       for (int r = 0; r < 16; r += 2) {
-        const float p0 = fast_exp2(sc[r] - m_use), p1 = fast_exp2(sc[r + 1] - m_use);
+        const float p0 = ALIBI ? fast_exp2(sc[r] - m_use) : fast_exp2(fmaf(sc[r], sc2, -m_use));
+        const float p1 = ALIBI ? fast_exp2(sc[r + 1] - m_use) : fast_exp2(fmaf(sc[r + 1], sc2, -m_use));
         psum += p0 + p1;
         pk[r >> 1] = T::pack2(p0, p1);
       }
@@ -177,21 +189,17 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecArgs a) {
       }
       __asm__ volatile("" ::: "memory");
     }
-#pragma unroll
-    for (int kk = 0; kk < KK; ++kk) kr[kk] = kn[kk];
-#pragma unroll
-    for (int u = 0; u < VCH; ++u) vr[u] = vn[u];
   }
 
   // Merge the four waves' states through LDS (reusing the V slots).
-  const float l_tot = l_run + swap_halves(l_run);
+  const float l_tot = sum_halves(l_run);
   __syncthreads();
   float* mg = (float*)smem;
   constexpr int MREG = (2 + D) * 32;
   if (w > 0) {
     float* r = mg + (w - 1) * MREG;
     if (g == 0) {
-      r[li] = m_run;
+      r[li] = m_ref;
       r[32 + li] = l_tot;
     }
 #pragma unroll
@@ -201,11 +209,11 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecArgs a) {
   }
   __syncthreads();
   if (w == 0) {
-    float M = m_run;
+    float M = m_ref;
 #pragma unroll
     for (int x = 0; x < 3; ++x) M = fmaxf(M, mg[x * MREG + li]);
     const float Mu = M == kNegInf ? 0.f : M;
-    const float s0 = fast_exp2(m_run - Mu);
+    const float s0 = fast_exp2(m_ref - Mu);
     float L = s0 * l_tot;
 #pragma unroll
     for (int db = 0; db < DB; ++db) o[db] *= s0;
@@ -245,26 +253,58 @@ struct MergeArgs {
   int splits;
 };
 
-// One workgroup of D threads per (batch, query head); thread d owns column d.
+// One workgroup of 256 threads per (batch, query head).  The split weights
+// exp(lse_s - M) / sum are formed once in LDS; then thread (column d, lane
+// group sg) sums its share of splits and the groups are added through LDS.
 template <class T, int D>
-__global__ __launch_bounds__(D) void decode_merge_kernel(MergeArgs a) {
-  const int bh = blockIdx.x, d = threadIdx.x;
+__global__ __launch_bounds__(256) void decode_merge_kernel(MergeArgs a) {
+  constexpr int NG = 256 / D;
+  __shared__ float wts[256];
+  __shared__ float red[256];
+  __shared__ float part[NG][D];
+  const int bh = blockIdx.x, t = threadIdx.x;
   const float* L = a.ws_lse + (size_t)bh * a.splits;
-  const float* O = a.ws_o + (size_t)bh * a.splits * D + d;
-  float M = kNegInf;
-  for (int x = 0; x < a.splits; ++x) M = fmaxf(M, L[x]);
-  float tot = 0.f, acc = 0.f;
-  if (M != kNegInf) {
-    for (int x = 0; x < a.splits; ++x) {
-      const float wgt = fast_exp2((L[x] - M) * kLog2e);
-      tot += wgt;
-      acc = fmaf(wgt, O[(size_t)x * D], acc);
-    }
+  const float lv = t < a.splits ? L[t] : kNegInf;
+  red[t] = lv;
+  __syncthreads();
+  for (int off = 128; off > 0; off >>= 1) {
+    if (t < off) red[t] = fmaxf(red[t], red[t + off]);
+    __syncthreads();
   }
-  const float val = tot > 0.f ? acc / tot : 0.f;
-  const uint32_t pr = T::pack2(val, 0.f);
-  a.out[(size_t)bh * D + d] = (uint16_t)(pr & 0xffffu);
-  if (d == 0 && a.lse) a.lse[bh] = tot > 0.f ? M + __logf(tot) : kNegInf;
+  const float M = red[0];
+  __syncthreads();
+  const float wv = (M == kNegInf || t >= a.splits) ? 0.f : fast_exp2((lv - M) * kLog2e);
+  wts[t] = wv;
+  red[t] = wv;
+  __syncthreads();
+  for (int off = 128; off > 0; off >>= 1) {
+    if (t < off) red[t] += red[t + off];
+    __syncthreads();
+  }
+  const float tot = red[0];
+  const int d = t % D, sg = t / D;
+  const float* O = a.ws_o + (size_t)bh * a.splits * D + d;
+  float acc = 0.f;
+  int x = sg;
+  for (; x + 3 * NG < a.splits; x += 4 * NG) {
+    const float o0 = O[(size_t)x * D], o1 = O[(size_t)(x + NG) * D];
+    const float o2 = O[(size_t)(x + 2 * NG) * D], o3 = O[(size_t)(x + 3 * NG) * D];
+    acc = fmaf(wts[x], o0, acc);
+    acc = fmaf(wts[x + NG], o1, acc);
+    acc = fmaf(wts[x + 2 * NG], o2, acc);
+    acc = fmaf(wts[x + 3 * NG], o3, acc);
+  }
+  for (; x < a.splits; x += NG) acc = fmaf(wts[x], O[(size_t)x * D], acc);
+  part[sg][d] = acc;
+  __syncthreads();
+  if (sg == 0) {
+    float sum = 0.f;
+#pragma unroll
+    for (int q = 0; q < NG; ++q) sum += part[q][d];
+    const float val = tot > 0.f ? sum / tot : 0.f;
+    a.out[(size_t)bh * D + d] = (uint16_t)(T::pack2(val, 0.f) & 0xffffu);
+    if (d == 0 && a.lse) a.lse[bh] = tot > 0.f ? M + __logf(tot) : kNegInf;
+  }
 }
 
 }  // namespace sa

@@ -64,7 +64,7 @@ void dispatch_fwd(const FwdArgs& args, bool causal, bool mask, bool alibi, hipSt
 template <class T, int D, bool M, bool A>
 void launch_decode(const DecArgs& args, const MergeArgs& margs, int nwg, int nbh, hipStream_t st) {
   hipLaunchKernelGGL((decode_split_kernel<T, D, M, A>), dim3(nwg), dim3(256), 0, st, args);
-  hipLaunchKernelGGL((decode_merge_kernel<T, D>), dim3(nbh), dim3(D), 0, st, margs);
+  hipLaunchKernelGGL((decode_merge_kernel<T, D>), dim3(nbh), dim3(256), 0, st, margs);
 }
 
 template <class T, int D>

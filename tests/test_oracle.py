@@ -303,7 +303,7 @@ def test_rows_subset_matches_full():
 def test_overflow_inputs_stay_finite():
     """Scores far beyond the fp16 range: the float64 oracle stays finite and exact."""
     w = Workload("big", 1, 20, 20, 2, 2, 64, "fp16", causal=True, seed=3)
-    inp = make_inputs(w, scale_values=64.0)
+    inp = make_inputs(w, scale_qk=64.0)
     q, k = to_f64(inp.q), to_f64(inp.k)
     assert np.abs(np.einsum("bihd,bjhd->bhij", q, k)).max() > 65504
     o, l = oracle.attention(q, k, to_f64(inp.v), w.scale, causal=True)

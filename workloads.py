@@ -91,19 +91,19 @@ class Inputs:
     tails: list = field(default_factory=list)
 
 
-def make_inputs(w: Workload, seed: Optional[int] = None, scale_values: float = 1.0) -> Inputs:
+def make_inputs(w: Workload, seed: Optional[int] = None, scale_qk: float = 1.0) -> Inputs:
     """CPU tensors for workload ``w`` (seed defaults to the workload's own).
 
-    ``scale_values`` multiplies the float32 draws before the cast, which the
-    overflow cases use to push ``q . k`` past the fp16 range.
+    ``scale_qk`` multiplies the float32 draws of q and k before the cast,
+    which the overflow cases use to push ``q . k`` past the fp16 range.
     """
     g = torch.Generator().manual_seed(w.seed if seed is None else seed)
     dt = DTYPES[w.dtype]
     q = torch.randn((w.B, w.S_q, w.H_q, w.D), generator=g)
     k = torch.randn((w.B, w.S_k, w.H_kv, w.D), generator=g)
     v = torch.randn((w.B, w.S_k, w.H_kv, w.D), generator=g)
-    if scale_values != 1.0:
-        q, k, v = q * scale_values, k * scale_values, v * scale_values
+    if scale_qk != 1.0:
+        q, k = q * scale_qk, k * scale_qk
     q, k, v = q.to(dt), k.to(dt), v.to(dt)
     mask = None
     tails = []
