@@ -183,6 +183,24 @@ def cpu_baseline(parts, budget_s):
             "sample": "; ".join(samples) + f" ({secs:.1f} s of float64 numpy)"}
 
 
+def copy_calibration(args, dev):
+    """A plain copy of known size: reads and writes exactly copy_mib MiB each."""
+    import torch
+    n = args.copy_mib << 20
+    src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(args.warmup):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    dt = (time.perf_counter() - t0) / args.steps
+    print(json.dumps({"copy_bytes": n, "ms_per_copy": round(dt * 1e3, 4),
+                      "read_plus_write_GBs": round(2 * n / dt / 1e9, 1)}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -191,6 +209,9 @@ def main():
     ap.add_argument("--workload", default="c5+c4", choices=sorted(STEPS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
+    ap.add_argument("--copy-mib", type=int, default=0,
+                    help="instead of the hot path, time a plain device-to-device copy of this many "
+                         "MiB (the reference kernel for scaling HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on exactly one GPU (asked for {args.gpus}); multi-GPU sharding is "
@@ -200,6 +221,9 @@ def main():
     import torch
     assert torch.cuda.is_available(), "no GPU visible"
     dev = torch.device("cuda:0")
+    if args.copy_mib:
+        copy_calibration(args, dev)
+        return
     parts = [Part(n, dev) for n in STEPS[args.workload]]
     stream = torch.cuda.current_stream(dev)
 

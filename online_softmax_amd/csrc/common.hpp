@@ -73,20 +73,38 @@ __device__ inline u32x2 lds_read_tr(const uint16_t* p) {
   return __builtin_bit_cast(u32x2, r);
 }
 
-// Buffer resource over [base, base + bytes): loads beyond the end read zero.
-__device__ inline __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, 0x00020000);
+// Buffer resource (V#) over [base, base + bytes): loads beyond the end read
+// zero.  Word 3 selects raw 32-bit data with no swizzle or stride.
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+__device__ inline i32x4 buffer_rsrc(const void* base, uint32_t bytes) {
+  const uint64_t a = (uint64_t)base;
+  return (i32x4){(int)(uint32_t)a, (int)((uint32_t)(a >> 32) & 0xffffu), (int)bytes, 0x00020000};
 }
 
 // Direct global-to-LDS copy of 16 bytes per lane: lane l's bytes land at
-// lds + 16 l (lds must be the same for the whole wave).
-__device__ inline void load_lds16(__amdgpu_buffer_rsrc_t r, void* lds, uint32_t voffset) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16, voffset, 0, 0, 0);
+// lds + 16 l (lds must be the same for the whole wave).  Written as inline
+// assembly so that the compiler does not treat later LDS reads of other
+// buffers as dependent on the copy (it would wait for every copy before
+// them); completion is awaited explicitly with wait_vmem() before the
+// barrier that publishes the buffer.  The copy has no register results; M0
+// carries the LDS base and needs one wait state before the load.
+__device__ inline void load_lds16(i32x4 rsrc, const void* lds, uint32_t voffset) {
+  const uint32_t lds_addr = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void*)lds;
+  __asm__ volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+                   :: "s"(lds_addr), "v"(voffset), "s"(rsrc) : "m0");
 }
 
 // Wait for this wave's outstanding vector-memory operations, including
 // global-to-LDS copies (vmcnt(0); the other counters are left alone).
 __device__ inline void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0f70); }
+
+// Wait until at most N of this wave's vector-memory operations are in flight
+// (they complete in issue order, so everything older than the last N is done).
+template <int N>
+__device__ inline void wait_vmem_n() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt(0x0f70 | (N & 15) | ((N >> 4) << 14));
+}
 
 // Workgroups are dealt to the eight XCDs round-robin (id % 8).  Renumber them
 // so that each XCD receives one contiguous run of work items, keeping the

@@ -76,6 +76,8 @@ int check_fwd(const FwdShape& s, bool* noop) {
   if (st != SA_OK) return st;
   if (s.S_q < 0) return fail(SA_ERR_INVALID_ARG, "negative S_q=%d", s.S_q);
   if (s.causal != 0 && s.causal != 1) return fail(SA_ERR_INVALID_ARG, "causal must be 0 or 1");
+  if (s.slopes && s.scale == 0.f)
+    return fail(SA_ERR_INVALID_ARG, "scale must be nonzero when ALiBi slopes are given");
   if (s.B == 0 || s.S_q == 0) { *noop = true; return SA_OK; }
   int64_t nq = 1, nk = 1;
   if (!mul_ok(&nq, s.B) || !mul_ok(&nq, s.S_q) || !mul_ok(&nq, s.H_q) || !mul_ok(&nq, s.D) ||
@@ -83,6 +85,9 @@ int check_fwd(const FwdShape& s, bool* noop) {
     return fail(SA_ERR_INVALID_ARG, "tensor sizes overflow");
   // Workgroups: B * H_q * ceil(S_q / 128) must fit a 1-D grid.
   int64_t items = (int64_t)s.B * s.H_q * ((s.S_q + 127) / 128);
+  // One key/value tile (64 rows) must be addressable by a 32-bit buffer range.
+  if ((int64_t)64 * s.H_kv * s.D * 2 >= (INT64_C(1) << 32))
+    return fail(SA_ERR_UNSUPPORTED, "H_kv * D too large for the tile copies");
   if (items > INT32_MAX) return fail(SA_ERR_INVALID_ARG, "too many query blocks (%lld)", (long long)items);
   if (!s.q || !s.out) return fail(SA_ERR_INVALID_ARG, "q and out must not be NULL");
   if (s.S_k > 0 && (!s.k || !s.v)) return fail(SA_ERR_INVALID_ARG, "k and v must not be NULL when S_k > 0");
@@ -117,6 +122,12 @@ int decode_num_splits(int B, int S_k, int H_q, int H_kv, int num_cu) {
   // Round to whole steps per split, then drop splits that would be empty.
   const int chunk = decode_chunk(S_k, (int)splits);
   return (S_k + chunk - 1) / chunk;
+}
+
+int fwd_waves(int B, int S_q, int H_q, bool causal, int num_cu) {
+  const int64_t wg8 = (int64_t)B * H_q * ((S_q + 255) / 256);
+  const int64_t need = (int64_t)(num_cu > 0 ? num_cu : 1) * (causal ? 4 : 1);
+  return wg8 >= need ? 8 : 4;
 }
 
 int decode_chunk(int S_k, int splits) {

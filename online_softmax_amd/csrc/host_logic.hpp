@@ -40,6 +40,11 @@ int check_fwd(const FwdShape& s, bool* noop);
 int check_decode(const DecodeShape& s, bool* noop);
 
 int decode_num_splits(int B, int S_k, int H_q, int H_kv, int num_cu);
+// Waves per prefill workgroup (4 or 8; a workgroup owns 32 query rows per
+// wave).  Eight-wave workgroups halve the key/value copy traffic per FLOP;
+// they are used when there are enough of them to keep every CU busy (for
+// causal work, enough to balance the unequal blocks).
+int fwd_waves(int B, int S_q, int H_q, bool causal, int num_cu);
 // Keys per split for a split count (a multiple of kDecodeStepKeys).
 int decode_chunk(int S_k, int splits);
 size_t decode_workspace_size(int B, int H_q, int S_k, int D);

@@ -7,13 +7,13 @@
 // finish with numerator / denominator and lse = max + log(denominator).
 //
 // Mapping onto gfx950:
-//  * a workgroup of four waves owns 128 query rows of one (batch, head); each
-//    wave owns 32 rows and keeps their Q slice in registers for the whole sweep;
+//  * a workgroup of NW waves (4 or 8) owns 32·NW query rows of one (batch,
+//    head); each wave owns 32 rows and keeps their Q slice in registers;
 //  * key/value tiles of 64 rows are copied from global memory straight into
-//    LDS (buffer loads with the LDS destination, 16 bytes per lane), double-
-//    buffered: the copies for tile t+1 are issued before tile t is computed
-//    and land in the other buffer, so one barrier per tile suffices; the
-//    buffer bounds return zeros past the last key;
+//    LDS (buffer loads with the LDS destination, 16 bytes per lane) through a
+//    ring of NS buffers per tensor; the buffer bounds return zeros past the
+//    last key.  Copies are issued NS-2 iterations ahead of the barrier that
+//    publishes them and awaited with a partial vmcnt;
 //  * LDS rows are unpadded; 16-byte chunks are placed at (chunk XOR f(row))
 //    so that the K reads (16 rows, one chunk) and the transposed V reads
 //    (4 consecutive rows, 4 chunks) each touch distinct banks;
@@ -23,11 +23,17 @@
 //    one exchange between the wave halves, and the probabilities already sit
 //    in the B-operand layout of the next product O^T += V^T P^T;
 //  * V stays row-major in LDS and is read transposed with ds_read_b64_tr_b16;
+//  * software pipeline: iteration t runs S^T of tile t+1 on the matrix cores
+//    while the vector units form the probabilities of tile t, then P·V of
+//    tile t, then prepares tile t+1;
 //  * exponentials are base 2 on the hardware exp unit with log2(e) folded into
-//    the score scale; the running maximum lives in that base-2 domain;
-//  * tiles that no rule hides any key of (the bulk of the sweep) take a path
-//    without masking arithmetic; tiles on the causal diagonal, the ragged end
-//    of the keys or with hidden padded keys take the masked path;
+//    the score scale; the running maximum lives in that base-2 domain.  The
+//    ALiBi bias (divided by the scale) is the initial value of the S^T
+//    accumulator, so scores with and without bias share one softmax path;
+//  * tiles that no rule hides any key of (the bulk of the sweep) skip the
+//    masking pass; tiles on the causal diagonal, at the ragged end of the
+//    keys or with padded keys take it.  Which tiles are free of padding is
+//    worked out once per workgroup into a bit per tile;
 //  * the reference maximum is raised only when a tile's maximum exceeds it by
 //    more than kRescaleSlack (base 2): the final out = numerator / denominator
 //    and lse = reference + log(denominator) are exact for any reference, and
@@ -39,6 +45,9 @@
 namespace sa {
 
 constexpr float kRescaleSlack = 8.0f;
+// Tiles whose padding bits a workgroup records (beyond this every tile takes
+// the masking pass, which stays correct).
+constexpr int kMaskFlagTiles = 4096;
 
 struct FwdArgs {
   const uint16_t* q;
@@ -50,7 +59,8 @@ struct FwdArgs {
   const float* slopes;
   int B, S_q, S_k, H_q, H_kv, G;
   float scale2;  // scale * log2(e)
-  int nmb;       // query blocks of 128 rows per (batch, head)
+  float alibi2;  // log2(e) / |scale log2(e)| = 1 / |scale|: bias to accumulator units
+  int nmb;       // query blocks per (batch, head)
   int nitems;    // B * H_q * nmb
 };
 
@@ -61,17 +71,19 @@ __device__ inline int lds_swizzle(int r) {
   else return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);
 }
 
-template <class T, int D, bool CAUSAL, bool MASK, bool ALIBI>
-__global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
-  constexpr int BM = 128;            // query rows per workgroup
+template <class T, int D, bool CAUSAL, bool MASK, bool ALIBI, int NW>
+__global__ __launch_bounds__(NW * 64, 2) void fwd_kernel(FwdArgs a) {
+  constexpr int BM = 32 * NW;        // query rows per workgroup
   constexpr int BN = 64;             // keys per tile
+  constexpr int NS = 2;  // LDS buffers per tensor
   constexpr int KK = D / 16;         // MFMA k-steps over the head dimension
   constexpr int DB = D / 32;         // 32-row blocks of O^T
-  constexpr int NI = BN * D / 2048;  // 1 KiB copies per wave per tensor per tile
+  constexpr int NI = BN * D * 2 / 1024 / NW;  // 1 KiB copies per wave per tensor per tile
+  static_assert(NI >= 1, "tile too small for the copy layout");
 
-  __shared__ __attribute__((aligned(1024))) uint16_t Ks[2][BN * D];
-  __shared__ __attribute__((aligned(1024))) uint16_t Vs[2][BN * D];
-  __shared__ uint32_t Ms[2][BN / 4];
+  __shared__ __attribute__((aligned(1024))) uint16_t Ks[NS][BN * D];
+  __shared__ __attribute__((aligned(1024))) uint16_t Vs[NS][BN * D];
+  __shared__ uint32_t Mf[MASK ? kMaskFlagTiles / 32 : 1];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -91,6 +103,46 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
   if (CAUSAL) n_end = min(n_end, m0 + BM + off);
   const int nt = n_end > 0 ? (n_end + BN - 1) / BN : 0;
 
+  const size_t rs = (size_t)a.H_kv * D;  // key/value row stride
+  const uint16_t* kb = a.k + ((size_t)b * a.S_k * a.H_kv + hk) * D;
+  const uint16_t* vb = a.v + ((size_t)b * a.S_k * a.H_kv + hk) * D;
+  const uint8_t* mrow = MASK ? a.mask + (size_t)b * a.S_k : nullptr;
+
+  // Copy u of this wave fills LDS bytes [cb KiB, cb KiB + 1 KiB) of a buffer,
+  // cb = NW u + w; lane l's 16 bytes are LDS row r, position p, holding global
+  // chunk p ^ f(r).
+  uint32_t voff[NI];
+#pragma unroll
+  for (int u = 0; u < NI; ++u) {
+    const int byte = (NW * u + w) * 1024 + 16 * lane;
+    const int r = byte / (2 * D), p = (byte % (2 * D)) / 16;
+    voff[u] = (uint32_t)(r * rs * 2 + 16 * (p ^ lds_swizzle<D>(r)));
+  }
+  auto tile_rsrc = [&](const uint16_t* base, int n0) {
+    const int rows = min(BN, a.S_k - n0);
+    return buffer_rsrc(base + (size_t)n0 * rs, (uint32_t)((rows - 1) * rs * 2 + 2 * D));
+  };
+  auto issue_k = [&](int t) {
+    const auto r = tile_rsrc(kb, t * BN);
+    uint16_t* buf = Ks[t % NS];
+#pragma unroll
+    for (int u = 0; u < NI; ++u) load_lds16(r, buf + (NW * u + w) * 512, voff[u]);
+  };
+  auto issue_v = [&](int t) {
+    const auto r = tile_rsrc(vb, t * BN);
+    uint16_t* buf = Vs[t % NS];
+#pragma unroll
+    for (int u = 0; u < NI; ++u) load_lds16(r, buf + (NW * u + w) * 512, voff[u]);
+  };
+
+  // Prologue copies: K of tiles 0..NS-1, V of tiles 0..NS-2.
+#pragma unroll
+  for (int j = 0; j < NS; ++j)
+    if (j < nt) issue_k(j);
+#pragma unroll
+  for (int j = 0; j < NS - 1; ++j)
+    if (j < nt) issue_v(j);
+
   // Q^T as the B operand: lane (row li, half g) holds q[row][16kk + 8g .. +7].
   // A negative scale is applied as |scale| on negated Q (exact in fp16/bf16),
   // so the row maximum of the raw products is the maximum of the scaled ones.
@@ -104,49 +156,32 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
     for (int kk = 0; kk < KK; ++kk) {
       qreg[kk] = qvalid ? *(const u32x4*)(qp + 16 * kk) : (u32x4){0, 0, 0, 0};
       qreg[kk] ^= qflip;
+      // Keep the flipped values as the loop-invariant operands (otherwise the
+      // compiler re-applies the flip inside the key loop).
+      __asm__ volatile("" : "+v"(qreg[kk]));
     }
   }
 
-  const size_t rs = (size_t)a.H_kv * D;  // key/value row stride
-  const uint16_t* kb = a.k + ((size_t)b * a.S_k * a.H_kv + hk) * D;
-  const uint16_t* vb = a.v + ((size_t)b * a.S_k * a.H_kv + hk) * D;
-  const uint8_t* mrow = MASK ? a.mask + (size_t)b * a.S_k : nullptr;
-
-  // Copy u of this wave fills LDS bytes [cb KiB, cb KiB + 1 KiB), cb = 4u + w;
-  // lane l's 16 bytes are LDS row r, position p, holding global chunk p ^ f(r).
-  uint32_t voff[NI];
+  // One bit per tile: every key of the tile is kept by the padding mask.
+  // Each wave checks 16 tiles per round, four lanes of 16 keys per tile.
+  if (MASK) {
+    for (int x = tid; x < kMaskFlagTiles / 32; x += NW * 64) Mf[x] = 0;
+    __syncthreads();
+    const int ntf = min(nt, kMaskFlagTiles);
+    for (int t0 = 16 * w; t0 < ntf; t0 += 16 * NW) {
+      const int j0 = (t0 + (lane >> 2)) * BN + 16 * (lane & 3);
+      bool keep = true;
 #pragma unroll
-  for (int u = 0; u < NI; ++u) {
-    const int byte = (4 * u + w) * 1024 + 16 * lane;
-    const int r = byte / (2 * D), p = (byte % (2 * D)) / 16;
-    voff[u] = (uint32_t)(r * rs * 2 + 16 * (p ^ lds_swizzle<D>(r)));
-  }
-  auto issue_tile = [&](int n0, int buf) {
-    const int rows = min(BN, a.S_k - n0);
-    const uint32_t bytes = (uint32_t)((rows - 1) * rs * 2 + 2 * D);
-    const auto rk = buffer_rsrc(kb + (size_t)n0 * rs, bytes);
-    const auto rv = buffer_rsrc(vb + (size_t)n0 * rs, bytes);
-#pragma unroll
-    for (int u = 0; u < NI; ++u) {
-      load_lds16(rk, &Ks[buf][(4 * u + w) * 512], voff[u]);
-      load_lds16(rv, &Vs[buf][(4 * u + w) * 512], voff[u]);
-    }
-  };
-  uint32_t mst = 0;
-  auto load_mask = [&](int n0) {
-    if (MASK && tid < BN / 4) {
-      uint32_t m = 0;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int j = n0 + 4 * tid + e;
-        m |= (uint32_t)((j < a.S_k && mrow[j] != 0) ? 1u : 0u) << (8 * e);
+      for (int e = 0; e < 16; ++e) {
+        const int j = j0 + e;
+        keep = keep && j < a.S_k && mrow[j < a.S_k ? j : 0] != 0;
       }
-      mst = m;
+      const uint64_t bal = __builtin_amdgcn_ballot_w64(keep);
+      const bool tile_ok = lane < 16 && ((bal >> (4 * lane)) & 0xfull) == 0xfull && t0 + lane < ntf;
+      const uint64_t bits = __builtin_amdgcn_ballot_w64(tile_ok);
+      if (lane == 0 && bits) atomicOr(&Mf[t0 >> 5], (uint32_t)(bits & 0xffffu) << (t0 & 31));
     }
-  };
-  auto store_mask = [&](int buf) {
-    if (MASK && tid < BN / 4) Ms[buf][tid] = mst;
-  };
+  }
 
   float m_ref = kNegInf;  // reference maximum, base-2 domain (raised lazily)
   float l_run = 0.f;      // this lane's share of the running row sum
@@ -154,7 +189,8 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
 #pragma unroll
   for (int db = 0; db < DB; ++db) o[db] = (f32x16){};
 
-  const float slope2 = ALIBI ? a.slopes[h] * kLog2e : 0.f;
+  // ALiBi slope in accumulator units: bias / |scale| per unit distance.
+  const float slope_acc = ALIBI ? a.slopes[h] * a.alibi2 : 0.f;
   const int wrow0 = m0 + 32 * w;                       // first row of this wave
   const bool wave_active = wrow0 < a.S_q;
   const int wave_last = min(wrow0 + 31, a.S_q - 1) + off;  // furthest key the wave may see
@@ -174,67 +210,69 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
       vofs[q][db] = r * D + 8 * ((4 * db + (tr_col >> 3)) ^ lds_swizzle<D>(r)) + (tr_col & 7);
     }
 
-  // One tile: scores, softmax update and output accumulation.  MASKED selects
-  // the path that applies the causal rule, the end of the keys and the
-  // padding mask; otherwise every key of the tile is visible to every row.
-  auto tile = [&](auto masked_tag, const int buf, const int n0) {
-    constexpr bool MASKED = decltype(masked_tag)::value;
-    f32x16 s[2] = {(f32x16){}, (f32x16){}};
-#pragma unroll
-    for (int kk = 0; kk < KK; ++kk) {
-#pragma unroll
-      for (int jb = 0; jb < 2; ++jb) {
-        const u32x4 ak = *(const u32x4*)&Ks[buf][(32 * jb + li) * D + 8 * ((2 * kk + g) ^ ksw)];
-        s[jb] = T::mma(ak, qreg[kk], s[jb]);
-      }
-    }
-    // Register r of block jb holds key n0 + 32 jb + 8 (r/4) + 4 g + r%4.
-    uint32_t mw[2][4];
-    if (MASKED && MASK) {
-#pragma unroll
-      for (int jb = 0; jb < 2; ++jb)
-#pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) mw[jb][q4] = Ms[buf][8 * jb + 2 * q4 + g];
-    }
-    auto visible = [&](int jb, int r) {
-      const int kofs = 32 * jb + 8 * (r >> 2) + (r & 3);
-      const int kj = n0 + 4 * g + kofs;
-      bool vis = kj < a.S_k;
-      if (CAUSAL) vis = vis && kj <= ipos;
-      if (MASK) vis = vis && ((mw[jb][r >> 2] >> (8 * (r & 3))) & 0xffu) != 0;
-      return vis;
-    };
-    float tmax = kNegInf;
-    if (!ALIBI) {
-      // Raw products; the scale enters once, in the exponent's fma.
-#pragma unroll
-      for (int jb = 0; jb < 2; ++jb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          if (MASKED) s[jb][r] = visible(jb, r) ? s[jb][r] : kNegInf;
-          tmax = fmaxf(tmax, s[jb][r]);
-        }
-      tmax = max_halves(tmax) * sc2;
-    } else {
-      // Scaled score plus bias -slope * |ipos - key|.  Under the causal rule
-      // every visible key satisfies key <= ipos, so the bias is linear there.
-      const float rel0 = (float)(ipos - n0 - 4 * g);
-      const float bb = -slope2 * rel0;
+  // Sᵀ = K Qᵀ for the 64 keys of tile t (register r of block jb holds key
+  // n0 + 32 jb + 8 (r/4) + 4 g + r%4).  With ALiBi the accumulator starts at
+  // the bias in accumulator units, -slope |ipos - key| / |scale|; under the
+  // causal rule every visible key has key <= ipos, so it is linear there.
+  auto qk = [&](const int t, f32x16 (&s)[2]) {
+    const uint16_t* kbuf = Ks[t % NS];
+    if (ALIBI) {
+      const float rel = (float)(t * BN + 4 * g - ipos);  // key - ipos at r = 0, jb = 0
+      const float b0 = slope_acc * rel;
 #pragma unroll
       for (int jb = 0; jb < 2; ++jb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const float kofs = (float)(32 * jb + 8 * (r >> 2) + (r & 3));
-          const float bias = CAUSAL ? fmaf(slope2, kofs, bb) : -slope2 * __builtin_fabsf(rel0 - kofs);
-          float t = fmaf(s[jb][r], sc2, bias);
-          if (MASKED) t = visible(jb, r) ? t : kNegInf;
-          s[jb][r] = t;
-          tmax = fmaxf(tmax, t);
+          s[jb][r] = CAUSAL ? fmaf(slope_acc, kofs, b0) : -slope_acc * __builtin_fabsf(rel + kofs);
         }
-      tmax = max_halves(tmax);
+    } else {
+      s[0] = (f32x16){};
+      s[1] = (f32x16){};
     }
-    // Raise the reference maximum only when some row's tile maximum exceeds
-    // it by more than the slack; rows that need no change get alpha = 1.
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) {
+#pragma unroll
+      for (int jb = 0; jb < 2; ++jb) {
+        const u32x4 ak = *(const u32x4*)&kbuf[(32 * jb + li) * D + 8 * ((2 * kk + g) ^ ksw)];
+        s[jb] = T::mma(ak, qreg[kk], s[jb]);
+      }
+    }
+  };
+
+  // Visibility and the running-maximum update for tile t.  Keys past the
+  // causal diagonal, past the end of the keys or cleared in the padding mask
+  // are set to -inf in a pass that only tiles touching them take (`masked`
+  // is uniform over the wave).  The scale enters once, in the exponent's fma,
+  // and the maximum is taken before scaling.  The reference maximum is raised
+  // only when some row's tile maximum exceeds it by more than the slack (rows
+  // that need no change get alpha = 1).
+  auto prepare = [&](const int t, f32x16 (&s)[2]) {
+    const int n0 = t * BN;
+    bool masked = n0 + BN > a.S_k || (CAUSAL && n0 + BN - 1 > wrow0 + off);
+    bool pad_free = true;
+    if (MASK) {
+      pad_free = t < kMaskFlagTiles && ((Mf[t >> 5] >> (t & 31)) & 1u);
+      masked = masked || !pad_free;
+    }
+    if (masked) {
+#pragma unroll
+      for (int jb = 0; jb < 2; ++jb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int kj = n0 + 4 * g + 32 * jb + 8 * (r >> 2) + (r & 3);
+          bool vis = kj < a.S_k;
+          if (CAUSAL) vis = vis && kj <= ipos;
+          if (MASK && !pad_free) vis = vis && mrow[vis ? kj : 0] != 0;
+          s[jb][r] = vis ? s[jb][r] : kNegInf;
+        }
+    }
+    float tmax = kNegInf;
+#pragma unroll
+    for (int jb = 0; jb < 2; ++jb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) tmax = fmaxf(tmax, s[jb][r]);
+    tmax = max_halves(tmax) * sc2;
     if (wave_any(tmax > m_ref + kRescaleSlack)) {
       const float m_new = fmaxf(m_ref, tmax);
       const float alpha = m_new == kNegInf ? 1.f : fast_exp2(m_ref - m_new);
@@ -243,36 +281,35 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
 #pragma unroll
       for (int db = 0; db < DB; ++db) o[db] *= alpha;
     }
-    // While a row has seen no visible key its reference is 0, so that no
-    // exp(-inf - (-inf)) is formed (only masked tiles can meet such a row).
-    const float m_use = (MASKED && m_ref == kNegInf) ? 0.f : m_ref;
-    const float nm = -m_use;
+  };
+
+  // Probabilities of a prepared tile, packed to the input type, and their sum.
+  // While a row has seen no visible key its reference is 0, so that no
+  // exp(-inf - (-inf)) is formed.
+  auto softmax_exp = [&](const f32x16 (&s)[2], uint32_t (&pk)[2][8]) {
+    const float nm = m_ref == kNegInf ? 0.f : -m_ref;
     float psum = 0.f;
-    uint32_t pk[2][8];
 #pragma unroll
     for (int jb = 0; jb < 2; ++jb) {
 #pragma unroll
       for (int r = 0; r < 16; r += 2) {
-        float p0, p1;
-        if (!ALIBI) {
-          p0 = fast_exp2(fmaf(s[jb][r], sc2, nm));
-          p1 = fast_exp2(fmaf(s[jb][r + 1], sc2, nm));
-        } else {
-          p0 = fast_exp2(s[jb][r] + nm);
-          p1 = fast_exp2(s[jb][r + 1] + nm);
-        }
+        const float p0 = fast_exp2(fmaf(s[jb][r], sc2, nm));
+        const float p1 = fast_exp2(fmaf(s[jb][r + 1], sc2, nm));
         psum += p0 + p1;
         pk[jb][r >> 1] = T::pack2(p0, p1);
       }
     }
     l_run += psum;
+  };
 
-    // O^T += V^T P^T over four 16-key steps.
+  // Oᵀ += Vᵀ Pᵀ over four 16-key steps of tile t.
+  auto pv = [&](const int t, const uint32_t (&pk)[2][8]) {
+    const uint16_t* vbuf = Vs[t % NS];
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
       const int jb = ks >> 1, mh = ks & 1;
       const u32x4 bp = {pk[jb][4 * mh], pk[jb][4 * mh + 1], pk[jb][4 * mh + 2], pk[jb][4 * mh + 3]};
-      const uint16_t* vt = &Vs[buf][16 * ks * D];
+      const uint16_t* vt = vbuf + 16 * ks * D;
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
         const u32x2 lo = lds_read_tr(vt + vofs[0][db]);
@@ -283,33 +320,106 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
     }
   };
 
-  if (nt > 0) {
-    issue_tile(0, 0);
-    load_mask(0);
-    store_mask(0);
-  }
+  // Instruction order for the block {Sᵀ of tile t+1, exponentials of tile t,
+  // P·V of tile t}: keep a few K reads ahead of the Sᵀ MFMAs and put the
+  // exponential work between them, so that neither the LDS latency nor the
+  // vector work leaves the matrix cores idle; then P·V with its transposed
+  // V reads two ahead.
+  auto interleave_schedule = [&]() {
+    constexpr int kMfma = 0x008, kValu = 0x002 | 0x400, kDsRead = 0x100;
+    constexpr int NQK = 2 * KK, NPV = 4 * DB;
+    __builtin_amdgcn_sched_group_barrier(kDsRead, 4, 0);
+#pragma unroll
+    for (int i = 0; i < NQK; ++i) {
+      __builtin_amdgcn_sched_group_barrier(kMfma, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(kValu, 5, 0);
+      if (i + 4 < NQK) __builtin_amdgcn_sched_group_barrier(kDsRead, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(kDsRead, 4, 0);
+#pragma unroll
+    for (int i = 0; i < NPV; ++i) {
+      __builtin_amdgcn_sched_group_barrier(kMfma, 1, 0);
+      if (i + 2 < NPV) __builtin_amdgcn_sched_group_barrier(kDsRead, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(kValu, 2, 0);
+    }
+  };
+
+  // Tiles this wave needs: all of them, or under the causal rule those that
+  // start at or before the wave's furthest visible key.
+  int ntw = wave_active ? nt : 0;
+  if (CAUSAL) ntw = wave_last < 0 ? 0 : min(ntw, wave_last / BN + 1);
+
+  // Iteration t issues K of tile t+NS (into the buffer K(t) left, whose Sᵀ
+  // was formed in iteration t-1) and V of tile t+NS-1 (into the buffer of
+  // V(t-1)).  Before the barrier that ends iteration t, K(t+2) and V(t+1)
+  // must have landed: they were issued NS-2 iterations earlier, so only the
+  // copies issued in this iteration may still be in flight.
+  auto copies = [&](const int t) -> int {
+    int n = 0;
+    if (t + NS < nt) {
+      issue_k(t + NS);
+      n += NI;
+    }
+    if (t + NS - 1 < nt) {
+      issue_v(t + NS - 1);
+      n += NI;
+    }
+    return n;
+  };
+  auto finish = [&](const int in_flight) {
+    if (NS == 2 || in_flight == 0) wait_vmem();
+    else if (in_flight == NI) wait_vmem_n<NI>();
+    else wait_vmem_n<2 * NI>();
+    __syncthreads();
+  };
+  // A full step: Sᵀ of tile t+1, probabilities and P·V of tile t, then the
+  // preparation of tile t+1.
+  auto full_step = [&](const int t, f32x16 (&s)[2], f32x16 (&sn)[2]) {
+    const int n = copies(t);
+    uint32_t pk[2][8];
+    qk(t + 1, sn);
+    softmax_exp(s, pk);
+    pv(t, pk);
+    interleave_schedule();
+    prepare(t + 1, sn);
+    finish(n);
+  };
+  // The wave's last tile: probabilities and P·V only.
+  auto last_step = [&](const int t, f32x16 (&s)[2]) {
+    const int n = copies(t);
+    uint32_t pk[2][8];
+    softmax_exp(s, pk);
+    pv(t, pk);
+    finish(n);
+  };
+
   wait_vmem();
   __syncthreads();
 
-  for (int t = 0; t < nt; ++t) {
-    const int buf = t & 1, n0 = t * BN;
-    if (t + 1 < nt) {
-      issue_tile(n0 + BN, buf ^ 1);
-      load_mask(n0 + BN);
-    }
-    const bool skip = !wave_active || (CAUSAL && n0 > wave_last);
-    if (!skip) {
-      bool fast = n0 + BN <= a.S_k && (!CAUSAL || n0 + BN - 1 <= wrow0 + off);
-      if (MASK && fast) fast = !wave_any(Ms[buf][lane & 15] != 0x01010101u);
-      if (fast)
-        tile(std::false_type{}, buf, n0);
-      else
-        tile(std::true_type{}, buf, n0);
-    }
-    if (t + 1 < nt) store_mask(buf ^ 1);
-    wait_vmem();
-    __syncthreads();
+  f32x16 sa[2], sb[2];
+  if (ntw > 0) {
+    qk(0, sa);
+    prepare(0, sa);
   }
+  // Iteration 0 overwrites the buffer of K(0): every wave must have read it.
+  __syncthreads();
+  int t = 0;
+  if (ntw > 0) {
+    for (; t + 2 < ntw; t += 2) {
+      full_step(t, sa, sb);
+      full_step(t + 1, sb, sa);
+    }
+    if (t + 1 < ntw) {
+      full_step(t, sa, sb);
+      last_step(t + 1, sb);
+      t += 2;
+    } else {
+      last_step(t, sa);
+      t += 1;
+    }
+  }
+  // Tiles this wave does not need still take part in the copies and barriers.
+  for (; t < nt; ++t) finish(copies(t));
 
   // Epilogue: out = O / l (0 for a row that saw no key), lse = ln of the sum.
   const float l_tot = sum_halves(l_run);

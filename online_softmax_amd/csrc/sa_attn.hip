@@ -5,6 +5,7 @@
 // instance for {dtype, D, causal, mask, ALiBi}, launch on the caller's stream.
 #include <hip/hip_runtime.h>
 
+#include <cmath>
 #include <mutex>
 
 #include "../../include/sa_attn.h"
@@ -42,22 +43,25 @@ int launched(const char* what) {
 }
 
 template <class T, int D, bool C, bool M, bool A>
-void launch_fwd(const FwdArgs& args, hipStream_t st) {
-  hipLaunchKernelGGL((fwd_kernel<T, D, C, M, A>), dim3(args.nitems), dim3(256), 0, st, args);
+void launch_fwd(const FwdArgs& args, int nw, hipStream_t st) {
+  if (nw == 8)
+    hipLaunchKernelGGL((fwd_kernel<T, D, C, M, A, 8>), dim3(args.nitems), dim3(512), 0, st, args);
+  else
+    hipLaunchKernelGGL((fwd_kernel<T, D, C, M, A, 4>), dim3(args.nitems), dim3(256), 0, st, args);
 }
 
 template <class T, int D>
-void dispatch_fwd(const FwdArgs& args, bool causal, bool mask, bool alibi, hipStream_t st) {
+void dispatch_fwd(const FwdArgs& args, bool causal, bool mask, bool alibi, int nw, hipStream_t st) {
   const int key = (causal ? 4 : 0) | (mask ? 2 : 0) | (alibi ? 1 : 0);
   switch (key) {
-    case 0: launch_fwd<T, D, false, false, false>(args, st); break;
-    case 1: launch_fwd<T, D, false, false, true>(args, st); break;
-    case 2: launch_fwd<T, D, false, true, false>(args, st); break;
-    case 3: launch_fwd<T, D, false, true, true>(args, st); break;
-    case 4: launch_fwd<T, D, true, false, false>(args, st); break;
-    case 5: launch_fwd<T, D, true, false, true>(args, st); break;
-    case 6: launch_fwd<T, D, true, true, false>(args, st); break;
-    default: launch_fwd<T, D, true, true, true>(args, st); break;
+    case 0: launch_fwd<T, D, false, false, false>(args, nw, st); break;
+    case 1: launch_fwd<T, D, false, false, true>(args, nw, st); break;
+    case 2: launch_fwd<T, D, false, true, false>(args, nw, st); break;
+    case 3: launch_fwd<T, D, false, true, true>(args, nw, st); break;
+    case 4: launch_fwd<T, D, true, false, false>(args, nw, st); break;
+    case 5: launch_fwd<T, D, true, false, true>(args, nw, st); break;
+    case 6: launch_fwd<T, D, true, true, false>(args, nw, st); break;
+    default: launch_fwd<T, D, true, true, true>(args, nw, st); break;
   }
 }
 
@@ -96,6 +100,11 @@ int sa_attn_fwd(const void* q, const void* k, const void* v, void* out, float* l
   int st = check_fwd(shp, &noop);
   if (st != SA_OK || noop) return st;
 
+  int cus = 0;
+  st = num_cus(&cus);
+  if (st != SA_OK) return st;
+  const int nw = fwd_waves(B, S_q, H_q, causal != 0, cus);
+
   FwdArgs args;
   args.q = (const uint16_t*)q;
   args.k = (const uint16_t*)k;
@@ -107,16 +116,17 @@ int sa_attn_fwd(const void* q, const void* k, const void* v, void* out, float* l
   args.B = B; args.S_q = S_q; args.S_k = S_k; args.H_q = H_q; args.H_kv = H_kv;
   args.G = H_q / H_kv;
   args.scale2 = scale * kLog2e;
-  args.nmb = (S_q + 127) / 128;
+  args.alibi2 = 1.0f / std::fabs(scale);
+  args.nmb = (S_q + 32 * nw - 1) / (32 * nw);
   args.nitems = B * H_q * args.nmb;
   const bool c = causal != 0, m = key_padding_mask != nullptr, al = alibi_slopes != nullptr;
   hipStream_t hs = (hipStream_t)stream;
   if (dtype == SA_F16) {
-    if (D == 64) dispatch_fwd<F16, 64>(args, c, m, al, hs);
-    else dispatch_fwd<F16, 128>(args, c, m, al, hs);
+    if (D == 64) dispatch_fwd<F16, 64>(args, c, m, al, nw, hs);
+    else dispatch_fwd<F16, 128>(args, c, m, al, nw, hs);
   } else {
-    if (D == 64) dispatch_fwd<BF16, 64>(args, c, m, al, hs);
-    else dispatch_fwd<BF16, 128>(args, c, m, al, hs);
+    if (D == 64) dispatch_fwd<BF16, 64>(args, c, m, al, nw, hs);
+    else dispatch_fwd<BF16, 128>(args, c, m, al, nw, hs);
   }
   return launched("attention forward");
 }
