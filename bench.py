@@ -43,7 +43,11 @@ MFMA_PEAK_TFLOPS = 2500.0   # MI355X dense fp16/bf16 matrix peak (published)
 HBM_PEAK_GBS = 8000.0       # MI355X HBM3E bandwidth (published)
 DECODE_ROTATION = 8
 PROFILES = ROOT / "profiles"
-KERNEL_SOURCES = ["common.hpp", "prefill.hpp", "decode.hpp", "sa_attn.hip"]
+# Sources each kernel is built from: a traffic figure measured on other sources is stale.
+KERNEL_SOURCES = {
+    "fwd_kernel": ["common.hpp", "prefill.hpp", "sa_attn.hip"],
+    "decode_split_kernel": ["common.hpp", "decode.hpp", "sa_attn.hip"],
+}
 
 STEPS = {
     "c5+c4": ["c5_alibi_8192", "c4_decode_32k"],
@@ -78,9 +82,9 @@ def kv_bytes(w):
     return 2 * w.B * w.S_k * w.H_kv * w.D * 2
 
 
-def source_sha():
+def source_sha(kernel):
     h = hashlib.sha256()
-    for n in KERNEL_SOURCES:
+    for n in KERNEL_SOURCES[kernel]:
         h.update((ROOT / "online_softmax_amd" / "csrc" / n).read_bytes())
     return h.hexdigest()[:16]
 
@@ -95,7 +99,7 @@ def read_traffic(kernel, workload):
         if ":" in line and not line.startswith("#"):
             a, b = line.split(":", 1)
             kv[a.strip()] = b.strip()
-    if kv.get("kernel_source_sha") != source_sha():
+    if kv.get("kernel_source_sha") != source_sha(kernel):
         return None
     try:
         return float(kv["hbm_bytes_per_launch"])
@@ -208,11 +212,16 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="c5+c4", choices=sorted(STEPS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--print-source-sha", action="store_true",
+                    help="print the source hash of each kernel (recorded with counter summaries) and exit")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="instead of the hot path, time a plain device-to-device copy of this many "
                          "MiB (the reference kernel for scaling HBM byte counters)")
     args = ap.parse_args()
+    if args.print_source_sha:
+        print(json.dumps({k: source_sha(k) for k in KERNEL_SOURCES}))
+        return
     if args.gpus != 1:
         print(f"bench.py runs on exactly one GPU (asked for {args.gpus}); multi-GPU sharding is "
               "not part of this build.", file=sys.stderr)
