@@ -94,13 +94,14 @@ size_t sa_attn_decode_workspace_size(int B, int H_q, int S_k, int D);
 
 /*
  * Single-token attention over a key/value cache (S_q = 1), split over the key
- * axis: each split streams its keys once for all H_q / H_kv query heads that
- * share a KV head and writes a normalised partial output and its log-sum-exp;
- * a second kernel merges the splits with log-sum-exp weights ("StreamAttention"
- * page, "Engine Direction": partial online-softmax states merged in a second
- * kernel; "Distributed and Long-Context Variants": log-sum-exp weighted
- * combining).  The result equals sa_attn_fwd with S_q = 1 (for which the
- * bottom-right causal rule hides nothing).
+ * axis: each split streams its keys once for up to 16 of the H_q / H_kv
+ * query heads that share a KV head and writes a normalised partial output and
+ * its log-sum-exp to the workspace; a second kernel merges the splits of each
+ * (batch, query head) with log-sum-exp weights into out and lse
+ * ("StreamAttention" page, "Engine Direction": partial online-softmax states
+ * merged in a second kernel; "Distributed and Long-Context Variants":
+ * log-sum-exp weighted combining).  The result equals sa_attn_fwd with
+ * S_q = 1 (for which the bottom-right causal rule hides nothing).
  *
  *   q        [B, 1, H_q, D]    dtype, device
  *   k_cache  [B, S_k, H_kv, D] dtype, device
@@ -112,9 +113,12 @@ size_t sa_attn_decode_workspace_size(int B, int H_q, int S_k, int D);
  *   workspace, workspace_bytes: caller-owned device scratch of at least
  *     sa_attn_decode_workspace_size(B, H_q, S_k, D) bytes, 16-byte aligned;
  *     its contents on entry do not matter and on return are unspecified.
+ *     Calls that may run at the same time must not share a workspace.
+ *   The scale must be nonzero when alibi_slopes is given.
  *
  * B == 0 is a no-op; S_k == 0 writes out = 0, lse = -inf.  Errors:
- * SA_ERR_INVALID_ARG, SA_ERR_UNSUPPORTED, SA_ERR_WORKSPACE, SA_ERR_HIP.
+ * SA_ERR_INVALID_ARG (also when one split would span 4 GiB or more of
+ * k_cache), SA_ERR_UNSUPPORTED, SA_ERR_WORKSPACE, SA_ERR_HIP.
  */
 int sa_attn_decode(const void* q, const void* k_cache, const void* v_cache,
                    void* out, float* lse, int B, int S_k, int H_q, int H_kv, int D,

@@ -162,7 +162,8 @@ def decode_num_splits(B: int, S_k: int, H_q: int, H_kv: int, num_cu: int) -> int
 
 
 def decode_workspace(B: int, H_q: int, S_k: int, D: int, device) -> torch.Tensor:
-    """A device byte buffer large enough for ``attn_decode`` at these sizes."""
+    """A device byte buffer large enough for ``attn_decode`` at these sizes
+    (reusable by calls issued one after another on a stream)."""
     n = decode_workspace_size(B, H_q, S_k, D)
     return torch.empty(max(n, 16), dtype=torch.uint8, device=device)
 

@@ -17,6 +17,7 @@ typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
@@ -30,6 +31,10 @@ struct F16 {
     return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
                                                   __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
   }
+  __device__ static inline f32x4 mma16(u32x4 a, u32x4 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a),
+                                                  __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+  }
   // Two floats to a packed pair, round to nearest even.
   __device__ static inline uint32_t pack2(float lo, float hi) {
     f32x2 v = {lo, hi};
@@ -40,6 +45,10 @@ struct F16 {
 struct BF16 {
   __device__ static inline f32x16 mma(u32x4 a, u32x4 b, f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+  }
+  __device__ static inline f32x4 mma16(u32x4 a, u32x4 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
                                                    __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
   }
   __device__ static inline uint32_t pack2(float lo, float hi) {
@@ -60,6 +69,18 @@ __device__ inline float max_halves(float x) {
 __device__ inline float sum_halves(float x) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Combine x over the four lanes l, l^16, l^32, l^48 (the lanes that hold one
+// query column of a 16x16 MFMA accumulator), with v_permlane16_swap and
+// v_permlane32_swap.
+__device__ inline float max_quarters(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return max_halves(fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1])));
+}
+__device__ inline float sum_quarters(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return sum_halves(__uint_as_float(r[0]) + __uint_as_float(r[1]));
 }
 
 // True in every lane when the predicate holds in any lane of the wave.
@@ -94,6 +115,27 @@ __device__ inline void load_lds16(i32x4 rsrc, const void* lds, uint32_t voffset)
                    :: "s"(lds_addr), "v"(voffset), "s"(rsrc) : "m0");
 }
 
+// The same resource in the form the buffer-load builtins take.
+__device__ inline __amdgpu_buffer_rsrc_t buffer_rsrc_t(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, 0x00020000);
+}
+
+// 16-byte buffer load into registers (zero past the end of the resource).
+__device__ inline u32x4 buffer_load16(__amdgpu_buffer_rsrc_t rsrc, uint32_t voffset, uint32_t soffset) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rsrc, voffset, soffset, 0));
+}
+
+// Device-coherent (sc1) 16-byte buffer store and load: they write through and
+// read past the per-XCD L2 caches, so workgroups on different XCDs see each
+// other's data once the store has completed, without cache-wide write-back
+// or invalidation.
+__device__ inline void buffer_store16_coherent(__amdgpu_buffer_rsrc_t rsrc, uint32_t voffset, u32x4 v) {
+  __builtin_amdgcn_raw_buffer_store_b128(v, rsrc, voffset, 0, 16);
+}
+__device__ inline u32x4 buffer_load16_coherent(__amdgpu_buffer_rsrc_t rsrc, uint32_t voffset) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rsrc, voffset, 0, 16));
+}
+
 // Wait for this wave's outstanding vector-memory operations, including
 // global-to-LDS copies (vmcnt(0); the other counters are left alone).
 __device__ inline void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0f70); }
@@ -104,6 +146,62 @@ template <int N>
 __device__ inline void wait_vmem_n() {
   static_assert(N >= 0 && N < 64, "vmcnt range");
   __builtin_amdgcn_s_waitcnt(0x0f70 | (N & 15) | ((N >> 4) << 14));
+}
+
+// wait_vmem_n for a count known only after loop unrolling (the switch folds
+// to one wait when n is a constant); counts past 47 wait for everything.
+__device__ inline void wait_vmem_upto(int n) {
+  switch (n) {
+    case 0: wait_vmem_n<0>(); break;
+    case 1: wait_vmem_n<1>(); break;
+    case 2: wait_vmem_n<2>(); break;
+    case 3: wait_vmem_n<3>(); break;
+    case 4: wait_vmem_n<4>(); break;
+    case 5: wait_vmem_n<5>(); break;
+    case 6: wait_vmem_n<6>(); break;
+    case 7: wait_vmem_n<7>(); break;
+    case 8: wait_vmem_n<8>(); break;
+    case 9: wait_vmem_n<9>(); break;
+    case 10: wait_vmem_n<10>(); break;
+    case 11: wait_vmem_n<11>(); break;
+    case 12: wait_vmem_n<12>(); break;
+    case 13: wait_vmem_n<13>(); break;
+    case 14: wait_vmem_n<14>(); break;
+    case 15: wait_vmem_n<15>(); break;
+    case 16: wait_vmem_n<16>(); break;
+    case 17: wait_vmem_n<17>(); break;
+    case 18: wait_vmem_n<18>(); break;
+    case 19: wait_vmem_n<19>(); break;
+    case 20: wait_vmem_n<20>(); break;
+    case 21: wait_vmem_n<21>(); break;
+    case 22: wait_vmem_n<22>(); break;
+    case 23: wait_vmem_n<23>(); break;
+    case 24: wait_vmem_n<24>(); break;
+    case 25: wait_vmem_n<25>(); break;
+    case 26: wait_vmem_n<26>(); break;
+    case 27: wait_vmem_n<27>(); break;
+    case 28: wait_vmem_n<28>(); break;
+    case 29: wait_vmem_n<29>(); break;
+    case 30: wait_vmem_n<30>(); break;
+    case 31: wait_vmem_n<31>(); break;
+    case 32: wait_vmem_n<32>(); break;
+    case 33: wait_vmem_n<33>(); break;
+    case 34: wait_vmem_n<34>(); break;
+    case 35: wait_vmem_n<35>(); break;
+    case 36: wait_vmem_n<36>(); break;
+    case 37: wait_vmem_n<37>(); break;
+    case 38: wait_vmem_n<38>(); break;
+    case 39: wait_vmem_n<39>(); break;
+    case 40: wait_vmem_n<40>(); break;
+    case 41: wait_vmem_n<41>(); break;
+    case 42: wait_vmem_n<42>(); break;
+    case 43: wait_vmem_n<43>(); break;
+    case 44: wait_vmem_n<44>(); break;
+    case 45: wait_vmem_n<45>(); break;
+    case 46: wait_vmem_n<46>(); break;
+    case 47: wait_vmem_n<47>(); break;
+    default: wait_vmem(); break;
+  }
 }
 
 // Workgroups are dealt to the eight XCDs round-robin (id % 8).  Renumber them

@@ -1,30 +1,37 @@
-// Decode kernels (one query token per sequence) over a key/value cache.
+// Decode kernel (one query token per sequence) over a key/value cache.
 //
-// Split phase: a workgroup owns one (batch, KV head, group of up to 32 query
-// heads sharing that KV head, key split).  Its four waves stream disjoint
-// 32-key sub-tiles of the split, so every key/value row is read from memory
-// once for all query heads of the group (the "StreamAttention" page, "Seed-Only
-// Serving Wedge" and "Engine Direction", argues against re-reading K/V per
-// query head under GQA).  Each wave keeps its own online-softmax state
-// (running maximum, running sum, unnormalised output) for the group's heads;
-// at the end the four states are merged through LDS and the split writes a
-// normalised partial output and its log-sum-exp.
+// A workgroup owns one (batch, KV head, group of up to 16 query heads sharing
+// that KV head, key split).  Its four waves stream disjoint 32-key sub-tiles
+// of the split, so every key/value row is read from memory once for all query
+// heads of the group (the "StreamAttention" page, "Seed-Only Serving Wedge"
+// and "Engine Direction", argues against re-reading K/V per query head under
+// GQA).  Each wave keeps its own online-softmax state (running maximum,
+// running sum, unnormalised output) for the group's heads; the four states are
+// merged through LDS and the split writes a normalised partial output and its
+// log-sum-exp to the workspace.
 //
-// Merge phase: one workgroup per (batch, query head) combines the splits with
-// log-sum-exp weights, the "partial online-softmax states merged in a second
-// kernel" of "Engine Direction" and the log-sum-exp weighted combining of
-// "Distributed and Long-Context Variants".
+// A second kernel combines the splits of every (batch, query head) with
+// log-sum-exp weights into the output: the "partial online-softmax states
+// merged" of the "StreamAttention" page, "Engine Direction", and the
+// "log-sum-exp weighted combining" of its "Distributed and Long-Context
+// Variants".  It is spread over one workgroup per (batch, query head, 16-wide
+// slice of D), so that it costs about one memory round trip.
 //
-// The matrix-core mapping is the prefill kernel's: S^T = K Q^T with the group's
-// query heads as the 32 MFMA columns (unused columns hold zero queries), then
-// O^T += V^T P^T with V read transposed from LDS.  K goes straight from global
-// memory into the A-operand registers (one key row per lane); V passes through
-// a wave-private LDS slot.  Each wave issues the loads of NSUB sub-tiles at
-// once before computing any of them, to keep many bytes in flight per CU.
+// Matrix-core mapping: 16x16x32 MFMAs with the group's query heads as the 16
+// columns: S^T = K Q^T (K straight from global memory into A-operand
+// registers, one key row per lane), then O^T += V^T P^T with V copied from
+// global memory into a wave-private LDS slot and read transposed with
+// ds_read_b64_tr_b16.  Each wave issues every copy and load of a round of
+// NSUB sub-tiles before computing any of them.
 #pragma once
 #include "common.hpp"
+#include "host_logic.hpp"
 
 namespace sa {
+
+// A wave rescales its state only when a sub-tile maximum exceeds the running
+// reference by more than this (base 2), bounding every probability by 2^8.
+constexpr float kDecodeSlack = 8.0f;
 
 struct DecArgs {
   const uint16_t* q;
@@ -32,180 +39,227 @@ struct DecArgs {
   const uint16_t* v;
   const uint8_t* mask;
   const float* slopes;
-  float* ws_o;    // [B, H_q, splits, D] normalised partial outputs
-  float* ws_lse;  // [B, H_q, splits] natural-log partial lse
+  uint16_t* out;      // [B, 1, H_q, D]
+  float* lse;         // [B, H_q, 1] or null
+  float* ws_o;        // [B, H_q, splits, D] normalised partial outputs
+  float* ws_lse;      // [B, H_q, splits] base-2 partial lse
   int B, S_k, H_q, H_kv, G, n_hg, splits, chunk;
-  float scale2;   // scale * log2(e)
+  float scale2;       // scale * log2(e)
+  float alibi2;       // 1 / |scale|: bias to accumulator units
 };
 
+// Chunk swizzle of a V row in a wave's LDS slot (16-byte chunks): spreads the
+// 16 rows x 32 bytes of one transposed read over the banks.
+template <int D>
+__device__ inline int dec_swizzle(int r) {
+  if constexpr (D == 128) return 2 * (r & 7);
+  else return 2 * ((r >> 1) & 3);
+}
+
 template <class T, int D, bool MASK, bool ALIBI>
-__global__ __launch_bounds__(256, 2) void decode_split_kernel(DecArgs a) {
-  constexpr int VSTR = D + 32;           // V row stride in LDS (16-bit words)
-  constexpr int KK = D / 16;
-  constexpr int DB = D / 32;
-  constexpr int VCH = 32 * D / 8 / 64;   // 16-byte V chunks per lane per 32-key sub-tile
-  constexpr int RCH = D / 8;
-  constexpr int NSUB = D == 64 ? 4 : 2;  // sub-tiles loaded together per wave
-  constexpr int VBYTES = 4 * 32 * VSTR * 2;
-  constexpr int MBYTES = 3 * (2 + D) * 32 * 4;
-  constexpr int SBYTES = VBYTES > MBYTES ? VBYTES : MBYTES;
-  __shared__ __attribute__((aligned(16))) unsigned char smem[SBYTES];
+__global__ __launch_bounds__(256, 2) void decode_kernel(DecArgs a) {
+  constexpr int KK = D / 32;             // MFMA k-steps (32 wide) over the head dimension
+  constexpr int DB = D / 16;             // 16-row blocks of O^T
+  constexpr int NSUB = D == 64 ? 4 : 2;  // 32-key sub-tiles per wave per round
+  constexpr int NK = 2 * KK;             // K loads per lane per sub-tile
+  constexpr int NV = 32 * D * 2 / 1024;  // 1 KiB V copies per wave per sub-tile
+  constexpr int SLOT = 32 * D;           // 16-bit words per sub-tile slot
+  constexpr int VBYTES = 4 * NSUB * SLOT * 2;
+  constexpr int MBYTES = 3 * (2 + D) * 16 * 4;
+  constexpr int FBYTES = 16 * kDecodeMaxSplits * 4 + 256 * 16;
+  constexpr int SB1 = VBYTES > MBYTES ? VBYTES : MBYTES;
+  constexpr int SBYTES = SB1 > FBYTES ? SB1 : FBYTES;
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[SBYTES];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int li = lane & 31, g = lane >> 5;
+  const int li = lane & 15, g4 = lane >> 4;
 
   const int s = blockIdx.x % a.splits;
-  int rest = blockIdx.x / a.splits;
-  const int hg = rest % a.n_hg;
-  rest /= a.n_hg;
-  const int hk = rest % a.H_kv;
-  const int b = rest / a.H_kv;
-  const int g_heads = min(32, a.G - 32 * hg);   // query heads in this group
-  const int h = hk * a.G + 32 * hg + li;         // this lane's query head
+  const int grp = blockIdx.x / a.splits;   // (b, hk, hg)
+  const int hg = grp % a.n_hg;
+  const int bk = grp / a.n_hg;
+  const int hk = bk % a.H_kv;
+  const int b = bk / a.H_kv;
+  const int g_heads = min(16, a.G - 16 * hg);   // query heads in this group
+  const int h0 = hk * a.G + 16 * hg;            // first query head of the group
+  const int h = h0 + li;                        // this lane's query head
   const bool hvalid = li < g_heads;
 
   const int k0 = s * a.chunk;
   const int k1 = min(a.S_k, k0 + a.chunk);
-  const int nsub_total = k1 > k0 ? (k1 - k0 + 31) / 32 : 0;   // 32-key sub-tiles in the split
-  const int nsteps = (nsub_total + 4 * NSUB - 1) / (4 * NSUB);
+  const int nsub = k1 > k0 ? (k1 - k0 + 31) / 32 : 0;   // 32-key sub-tiles in the split
+  const int rounds = (nsub + 4 * NSUB - 1) / (4 * NSUB);
   const int ipos = a.S_k - 1;  // the query's position on the key axis
 
+  // Q^T as the B operand: lane (column li, quarter g4) holds q[li][8 g4 + 32 kk .. +7].
   const uint32_t qflip = a.scale2 < 0.f ? 0x80008000u : 0u;
   const float sc2 = __builtin_fabsf(a.scale2);
   u32x4 qreg[KK];
   {
-    const uint16_t* qp = a.q + ((size_t)b * a.H_q + (hvalid ? h : 0)) * D + 8 * g;
+    const uint16_t* qp = a.q + ((size_t)b * a.H_q + (hvalid ? h : 0)) * D + 8 * g4;
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk) {
-      qreg[kk] = hvalid ? *(const u32x4*)(qp + 16 * kk) : (u32x4){0, 0, 0, 0};
+      qreg[kk] = hvalid ? *(const u32x4*)(qp + 32 * kk) : (u32x4){0, 0, 0, 0};
       qreg[kk] ^= qflip;
     }
   }
 
-  const size_t rs = (size_t)a.H_kv * D;
-  const uint16_t* kb = a.k + ((size_t)b * a.S_k * a.H_kv + hk) * D;
-  const uint16_t* vb = a.v + ((size_t)b * a.S_k * a.H_kv + hk) * D;
-  uint16_t* Vw = (uint16_t*)smem + w * 32 * VSTR;
+  // One buffer resource per split: rows past k1 read as zero.
+  const size_t rs = (size_t)a.H_kv * D;  // key/value row stride (16-bit words)
+  const size_t base = ((size_t)b * a.S_k * a.H_kv + hk) * D + (size_t)k0 * rs;
+  const uint32_t bytes = k1 > k0 ? (uint32_t)((size_t)(k1 - k0 - 1) * rs * 2 + 2 * D) : 0u;
+  const auto rk = buffer_rsrc_t(a.k + base, bytes);
+  const i32x4 rv = buffer_rsrc(a.v + base, bytes);
   const uint8_t* mrow = MASK ? a.mask + (size_t)b * a.S_k : nullptr;
 
-  float m_ref = kNegInf, l_run = 0.f;
-  f32x16 o[DB];
+  uint16_t* slots = (uint16_t*)smem + w * NSUB * SLOT;
+  // V copy c of a sub-tile: lane l's 16 bytes are LDS row r, position p of the
+  // slot, holding global chunk p ^ f(r) of key row r.
+  uint32_t vsrc[NV];
 #pragma unroll
-  for (int db = 0; db < DB; ++db) o[db] = (f32x16){};
-  const float slope2 = (ALIBI && hvalid) ? a.slopes[h] * kLog2e : 0.f;
-  const int tr_key = 4 * g + ((lane & 15) >> 2);
-  const int tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
-
-  for (int st = 0; st < nsteps; ++st) {
-    // Sub-tiles are dealt to the waves round-robin: sub-tile u = w + 4 (st NSUB + v).
-    u32x4 kr[NSUB][KK], vr[NSUB][VCH];
+  for (int c = 0; c < NV; ++c) {
+    const int byte = c * 1024 + 16 * lane;
+    const int r = byte / (2 * D), p = (byte % (2 * D)) / 16;
+    vsrc[c] = (uint32_t)(r * rs * 2 + 16 * (p ^ dec_swizzle<D>(r)));
+  }
+  // Transposed V read of key step hi (keys 16 hi + 4 g4 + t/4, t = lane % 16)
+  // and d block db (d = 16 db + 4 (t % 4)): word offset in a slot.
+  int vofs[2][DB];
 #pragma unroll
-    for (int v = 0; v < NSUB; ++v) {
-      const int base = k0 + 32 * (w + 4 * (st * NSUB + v));
-      const int j = base + li;
-      const bool ok = j < k1;
-      const uint16_t* kp = kb + (size_t)(ok ? j : k0) * rs + 8 * g;
+  for (int hi = 0; hi < 2; ++hi)
 #pragma unroll
-      for (int kk = 0; kk < KK; ++kk) {
-        kr[v][kk] = *(const u32x4*)(kp + 16 * kk);
-        if (!ok) kr[v][kk] = (u32x4){0, 0, 0, 0};
-      }
-#pragma unroll
-      for (int u = 0; u < VCH; ++u) {
-        const int c = lane + 64 * u, row = c / RCH, col = (c % RCH) * 8;
-        const bool okv = base + row < k1;
-        vr[v][u] = *(const u32x4*)(vb + (size_t)(okv ? base + row : k0) * rs + col);
-        if (!okv) vr[v][u] = (u32x4){0, 0, 0, 0};
-      }
+    for (int db = 0; db < DB; ++db) {
+      const int r = 16 * hi + 4 * g4 + (li >> 2);
+      const int d = 16 * db + 4 * (li & 3);
+      vofs[hi][db] = r * D + 8 * ((d >> 3) ^ dec_swizzle<D>(r)) + (d & 7);
     }
+
+  float m_ref = kNegInf, l_run = 0.f;
+  f32x4 o[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db) o[db] = (f32x4){};
+  const float slope_acc = (ALIBI && hvalid) ? a.slopes[h] * a.alibi2 : 0.f;
+
+  for (int rd = 0; rd < rounds; ++rd) {
+    // Sub-tile v of this round covers keys k0 + 32 u .. +31, u = w + 4 (NSUB rd + v).
+    // Copies of V go first, then the K loads, so that the wait for K(v) also
+    // covers V(v).
 #pragma unroll
     for (int v = 0; v < NSUB; ++v) {
-      const int base = k0 + 32 * (w + 4 * (st * NSUB + v));
-      if (base >= k1) break;  // wave-uniform
-      f32x16 sc = (f32x16){};
+      const uint32_t row0 = (uint32_t)(32 * (w + 4 * (NSUB * rd + v)));
 #pragma unroll
-      for (int kk = 0; kk < KK; ++kk) sc = T::mma(kr[v][kk], qreg[kk], sc);
-      // Stage this sub-tile's V rows in the wave's LDS slot.  LDS operations
-      // of one wave complete in order; the waits and compiler barriers keep
-      // the compiler from moving the reads of the previous sub-tile past
-      // these writes or these writes past the reads below.
-      __builtin_amdgcn_s_waitcnt(0xc07f);
-      __asm__ volatile("" ::: "memory");
+      for (int c = 0; c < NV; ++c)
+        load_lds16(rv, slots + v * SLOT + c * 512, vsrc[c] + row0 * (uint32_t)rs * 2);
+    }
+    u32x4 kr[NSUB][2][KK];
 #pragma unroll
-      for (int u = 0; u < VCH; ++u) {
-        const int c = lane + 64 * u, row = c / RCH, col = (c % RCH) * 8;
-        *(u32x4*)&Vw[row * VSTR + col] = vr[v][u];
+    for (int v = 0; v < NSUB; ++v) {
+      const uint32_t row0 = (uint32_t)(32 * (w + 4 * (NSUB * rd + v)));
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk)
+          kr[v][kb][kk] = buffer_load16(rk, (row0 + 16 * kb + li) * (uint32_t)rs * 2 + 2 * (8 * g4 + 32 * kk), 0);
+    }
+    // Keep every load of the round ahead of the first wait for one of them.
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int v = 0; v < NSUB; ++v) {
+      // Sub-tiles past the split's end are computed too (their keys read as
+      // zero and are masked out), so that the loads above stay where they are
+      // issued rather than being sunk behind a branch.
+      const int kbase = k0 + 32 * (w + 4 * (NSUB * rd + v));
+      // Sᵀ for keys kbase + 16 kb + 4 g4 + r (register r of block kb).  With
+      // ALiBi the accumulator starts at -slope (ipos - key) / |scale|.
+      f32x4 sc[2];
+      if (ALIBI) {
+        const float b0 = slope_acc * (float)(kbase + 4 * g4 - ipos);
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) sc[kb][r] = fmaf(slope_acc, (float)(16 * kb + r), b0);
+      } else {
+        sc[0] = (f32x4){};
+        sc[1] = (f32x4){};
       }
-      __builtin_amdgcn_s_waitcnt(0xc07f);
-      __asm__ volatile("" ::: "memory");
-
-      const bool need_mask = MASK || base + 32 > k1;
-      const float rel0 = (float)(ipos - base - 4 * g);
-      const float bb = -slope2 * rel0;
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk)
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) sc[kb] = T::mma16(kr[v][kb][kk], qreg[kk], sc[kb]);
+      if (MASK || kbase + 32 > k1) {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int kj = kbase + 16 * kb + 4 * g4 + r;
+            bool vis = kj < k1;
+            if (MASK) vis = vis && mrow[vis ? kj : 0] != 0;
+            sc[kb][r] = vis ? sc[kb][r] : kNegInf;
+          }
+      }
       float tmax = kNegInf;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int kofs = 8 * (r >> 2) + (r & 3);
-        float x = ALIBI ? fmaf(sc[r], sc2, fmaf(slope2, (float)kofs, bb)) : sc[r];
-        if (need_mask) {
-          const int kj = base + 4 * g + kofs;
-          bool vis = kj < k1;
-          if (MASK) vis = vis && mrow[vis ? kj : 0] != 0;
-          x = vis ? x : kNegInf;
-        }
-        sc[r] = x;
-        tmax = fmaxf(tmax, x);
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) tmax = fmaxf(tmax, sc[kb][r]);
+      tmax = max_quarters(tmax) * sc2;
+      if (wave_any(tmax > m_ref + kDecodeSlack)) {
+        const float m_new = fmaxf(m_ref, tmax);
+        const float alpha = m_new == kNegInf ? 1.f : fast_exp2(m_ref - m_new);
+        m_ref = m_new;
+        l_run *= alpha;
+#pragma unroll
+        for (int db = 0; db < DB; ++db) o[db] *= alpha;
       }
-      tmax = max_halves(tmax);
-      if (!ALIBI) tmax *= sc2;
-      const float m_new = fmaxf(m_ref, tmax);
-      const float m_use = m_new == kNegInf ? 0.f : m_new;
-      const float alpha = fast_exp2(m_ref - m_use);
-      m_ref = m_new;
+      const float nm = m_ref == kNegInf ? 0.f : -m_ref;
+      uint32_t pk[4];
       float psum = 0.f;
-      uint32_t pk[8];
 #pragma unroll
-      for (int r = 0; r < 16; r += 2) {
-        const float p0 = ALIBI ? fast_exp2(sc[r] - m_use) : fast_exp2(fmaf(sc[r], sc2, -m_use));
-        const float p1 = ALIBI ? fast_exp2(sc[r + 1] - m_use) : fast_exp2(fmaf(sc[r + 1], sc2, -m_use));
-        psum += p0 + p1;
-        pk[r >> 1] = T::pack2(p0, p1);
-      }
-      l_run = fmaf(l_run, alpha, psum);
+      for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int db = 0; db < DB; ++db) o[db] *= alpha;
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        const u32x4 bp = {pk[4 * ks], pk[4 * ks + 1], pk[4 * ks + 2], pk[4 * ks + 3]};
-        const uint16_t* vrow0 = &Vw[(16 * ks + tr_key) * VSTR + tr_col];
-#pragma unroll
-        for (int db = 0; db < DB; ++db) {
-          const u32x2 lo = lds_read_tr(vrow0 + 32 * db);
-          const u32x2 hi = lds_read_tr(vrow0 + 8 * VSTR + 32 * db);
-          const u32x4 av = {lo[0], lo[1], hi[0], hi[1]};
-          o[db] = T::mma(av, bp, o[db]);
+        for (int r = 0; r < 4; r += 2) {
+          const float p0 = fast_exp2(fmaf(sc[kb][r], sc2, nm));
+          const float p1 = fast_exp2(fmaf(sc[kb][r + 1], sc2, nm));
+          psum += p0 + p1;
+          pk[2 * kb + (r >> 1)] = T::pack2(p0, p1);
         }
-      }
+      l_run += psum;
+      // V(v) was copied before every K load of the round: once only the
+      // copies and loads issued after it are in flight, its slot is complete.
+      wait_vmem_upto((NSUB - 1 - v) * NV + NSUB * NK);
       __asm__ volatile("" ::: "memory");
+      const u32x4 bp = {pk[0], pk[1], pk[2], pk[3]};
+      const uint16_t* vs = slots + v * SLOT;
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        const u32x2 lo = lds_read_tr(vs + vofs[0][db]);
+        const u32x2 hi = lds_read_tr(vs + vofs[1][db]);
+        const u32x4 av = {lo[0], lo[1], hi[0], hi[1]};
+        o[db] = T::mma16(av, bp, o[db]);
+      }
     }
+    // The next round's copies reuse the slots: every transposed read of this
+    // round must have returned (they have: their results fed the MFMAs).
+    __asm__ volatile("" ::: "memory");
   }
 
   // Merge the four waves' states through LDS (reusing the V slots).
-  const float l_tot = sum_halves(l_run);
+  const float l_tot = sum_quarters(l_run);
+  wait_vmem();
   __syncthreads();
   float* mg = (float*)smem;
-  constexpr int MREG = (2 + D) * 32;
+  constexpr int MREG = (2 + D) * 16;
   if (w > 0) {
     float* r = mg + (w - 1) * MREG;
-    if (g == 0) {
+    if (g4 == 0) {
       r[li] = m_ref;
-      r[32 + li] = l_tot;
+      r[16 + li] = l_tot;
     }
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) r[64 + (32 * db + 8 * (e >> 2) + 4 * g + (e & 3)) * 32 + li] = o[db][e];
+      for (int e = 0; e < 4; ++e) r[32 + (16 * db + 4 * g4 + e) * 16 + li] = o[db][e];
   }
   __syncthreads();
   if (w == 0) {
@@ -221,89 +275,90 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(DecArgs a) {
     for (int x = 0; x < 3; ++x) {
       const float* r = mg + x * MREG;
       const float sx = fast_exp2(r[li] - Mu);
-      L = fmaf(sx, r[32 + li], L);
+      L = fmaf(sx, r[16 + li], L);
 #pragma unroll
       for (int db = 0; db < DB; ++db)
 #pragma unroll
-        for (int e = 0; e < 16; ++e)
-          o[db][e] = fmaf(sx, r[64 + (32 * db + 8 * (e >> 2) + 4 * g + (e & 3)) * 32 + li], o[db][e]);
+        for (int e = 0; e < 4; ++e) o[db][e] = fmaf(sx, r[32 + (16 * db + 4 * g4 + e) * 16 + li], o[db][e]);
     }
     if (hvalid) {
       const size_t idx = ((size_t)b * a.H_q + h) * a.splits + s;
       const float inv = L > 0.f ? 1.f / L : 0.f;
-      float* op = a.ws_o + idx * D + 4 * g;
+      float* op = a.ws_o + idx * D + 4 * g4;
 #pragma unroll
-      for (int db = 0; db < DB; ++db)
-#pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) {
-          const float4 v4 = {o[db][4 * q4] * inv, o[db][4 * q4 + 1] * inv, o[db][4 * q4 + 2] * inv,
-                             o[db][4 * q4 + 3] * inv};
-          *(float4*)(op + 32 * db + 8 * q4) = v4;
-        }
-      if (g == 0) a.ws_lse[idx] = L > 0.f ? (M + __log2f(L)) * kLn2 : kNegInf;
+      for (int db = 0; db < DB; ++db) *(f32x4*)(op + 16 * db) = o[db] * inv;
+      if (g4 == 0) a.ws_lse[idx] = L > 0.f ? M + __log2f(L) : kNegInf;
     }
   }
 }
 
 struct MergeArgs {
-  const float* ws_o;
-  const float* ws_lse;
-  uint16_t* out;   // [B, 1, H_q, D]
-  float* lse;      // [B, H_q, 1] or null
+  const float* ws_o;   // [B * H_q, splits, D]
+  const float* ws_lse; // [B * H_q, splits], base 2
+  uint16_t* out;       // [B * H_q, D]
+  float* lse;          // [B * H_q] or null
   int splits;
 };
 
-// One workgroup of 256 threads per (batch, query head).  The split weights
-// exp(lse_s - M) / sum are formed once in LDS; then thread (column d, lane
-// group sg) sums its share of splits and the groups are added through LDS.
+// One workgroup per (batch * query head, 16-wide slice of D): out = sum_s w_s
+// o_s / sum_s w_s with w_s = exp2(lse_s - max lse) (splits with lse_s = -inf
+// weigh nothing); lse = (max + log2 sum w) ln 2.  Thread t loads the 4-wide
+// d chunk t % 4 of split t / 4 (+ 64 x): every load of the workgroup is
+// issued before any is used.
 template <class T, int D>
 __global__ __launch_bounds__(256) void decode_merge_kernel(MergeArgs a) {
-  constexpr int NG = 256 / D;
-  __shared__ float wts[256];
-  __shared__ float red[256];
-  __shared__ float part[NG][D];
-  const int bh = blockIdx.x, t = threadIdx.x;
-  const float* L = a.ws_lse + (size_t)bh * a.splits;
-  const float lv = t < a.splits ? L[t] : kNegInf;
-  red[t] = lv;
-  __syncthreads();
-  for (int off = 128; off > 0; off >>= 1) {
-    if (t < off) red[t] = fmaxf(red[t], red[t + off]);
-    __syncthreads();
-  }
-  const float M = red[0];
-  __syncthreads();
-  const float wv = (M == kNegInf || t >= a.splits) ? 0.f : fast_exp2((lv - M) * kLog2e);
-  wts[t] = wv;
-  red[t] = wv;
-  __syncthreads();
-  for (int off = 128; off > 0; off >>= 1) {
-    if (t < off) red[t] += red[t + off];
-    __syncthreads();
-  }
-  const float tot = red[0];
-  const int d = t % D, sg = t / D;
-  const float* O = a.ws_o + (size_t)bh * a.splits * D + d;
-  float acc = 0.f;
-  int x = sg;
-  for (; x + 3 * NG < a.splits; x += 4 * NG) {
-    const float o0 = O[(size_t)x * D], o1 = O[(size_t)(x + NG) * D];
-    const float o2 = O[(size_t)(x + 2 * NG) * D], o3 = O[(size_t)(x + 3 * NG) * D];
-    acc = fmaf(wts[x], o0, acc);
-    acc = fmaf(wts[x + NG], o1, acc);
-    acc = fmaf(wts[x + 2 * NG], o2, acc);
-    acc = fmaf(wts[x + 3 * NG], o3, acc);
-  }
-  for (; x < a.splits; x += NG) acc = fmaf(wts[x], O[(size_t)x * D], acc);
-  part[sg][d] = acc;
-  __syncthreads();
-  if (sg == 0) {
-    float sum = 0.f;
+  constexpr int NX = kDecodeMaxSplits / 64;
+  __shared__ float s_w[kDecodeMaxSplits];
+  __shared__ float s_red[4][4];
+  __shared__ f32x4 s_acc[4][4];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int bh = blockIdx.x / (D / 16), slice = blockIdx.x % (D / 16);
+  const int ns = a.splits;
+  const float* lp = a.ws_lse + (size_t)bh * ns;
+  const float* op = a.ws_o + (size_t)bh * ns * D + 16 * slice + 4 * (tid & 3);
+  const float lv = tid < ns ? lp[tid] : kNegInf;
+  f32x4 ov[NX];
 #pragma unroll
-    for (int q = 0; q < NG; ++q) sum += part[q][d];
-    const float val = tot > 0.f ? sum / tot : 0.f;
-    a.out[(size_t)bh * D + d] = (uint16_t)(T::pack2(val, 0.f) & 0xffffu);
-    if (d == 0 && a.lse) a.lse[bh] = tot > 0.f ? M + __logf(tot) : kNegInf;
+  for (int x = 0; x < NX; ++x) {
+    const int sp = (tid >> 2) + 64 * x;
+    ov[x] = sp < ns ? *(const f32x4*)(op + (size_t)sp * D) : (f32x4){};
+  }
+  // Largest lse over the splits, then the weights and their sum.
+  float m = lv;
+#pragma unroll
+  for (int k = 32; k > 0; k >>= 1) m = fmaxf(m, __shfl_xor(m, k));
+  if (lane == 0) s_red[0][w] = m;
+  __syncthreads();
+  const float M = fmaxf(fmaxf(s_red[0][0], s_red[0][1]), fmaxf(s_red[0][2], s_red[0][3]));
+  const float wgt = fast_exp2(lv - (M == kNegInf ? 0.f : M));
+  if (tid < kDecodeMaxSplits) s_w[tid] = wgt;
+  float tot = wgt;
+#pragma unroll
+  for (int k = 32; k > 0; k >>= 1) tot += __shfl_xor(tot, k);
+  if (lane == 0) s_red[1][w] = tot;
+  __syncthreads();
+  tot = s_red[1][0] + s_red[1][1] + s_red[1][2] + s_red[1][3];
+  // Weighted sum over this thread's splits, then over the 16 threads of the
+  // wave that hold the same d chunk, then over the four waves.
+  f32x4 acc = {};
+#pragma unroll
+  for (int x = 0; x < NX; ++x) {
+    const int sp = (tid >> 2) + 64 * x;
+    acc += (sp < ns ? s_w[sp] : 0.f) * ov[x];
+  }
+#pragma unroll
+  for (int k = 32; k >= 4; k >>= 1)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) acc[e] += __shfl_xor(acc[e], k);
+  if (lane < 4) s_acc[w][lane] = acc;
+  __syncthreads();
+  if (tid < 4) {
+    const f32x4 sum = s_acc[0][tid] + s_acc[1][tid] + s_acc[2][tid] + s_acc[3][tid];
+    const float inv = tot > 0.f ? 1.f / tot : 0.f;
+    const uint2 pk = {T::pack2(sum[0] * inv, sum[1] * inv), T::pack2(sum[2] * inv, sum[3] * inv)};
+    *(uint2*)(a.out + (size_t)bh * D + 16 * slice + 4 * tid) = pk;
+    if (tid == 0 && slice == 0 && a.lse)
+      a.lse[bh] = tot > 0.f ? (M + __log2f(tot)) * kLn2 : kNegInf;
   }
 }
 

@@ -138,6 +138,23 @@ int decode_chunk(int S_k, int splits) {
   return steps * kDecodeStepKeys;
 }
 
+DecodeLayout decode_layout(int B, int H_q, int splits, int D) {
+  // Partial outputs [B, H_q, splits, D], then the partial lse
+  // [B, H_q, splits] from the next 256-byte boundary.
+  DecodeLayout l;
+  const int64_t n = (int64_t)B * H_q * splits;
+  l.o_offset = 0;
+  l.lse_offset = (n * D * 4 + 255) / 256 * 256;
+  l.bytes = l.lse_offset + n * 4;
+  return l;
+}
+
+bool decode_offsets_fit(int chunk, int H_kv, int D) {
+  // Byte offsets inside one split (including the rows past its end that a
+  // workgroup's last round addresses and reads as zero) are 32-bit.
+  return ((int64_t)chunk + kDecodeRoundKeys) * H_kv * D * 2 < ((int64_t)1 << 32);
+}
+
 size_t decode_workspace_size(int B, int H_q, int S_k, int D) {
   if (B < 0 || H_q < 0 || S_k < 0 || D < 0) return 0;
   int64_t max_splits = std::min<int64_t>(kDecodeMaxSplits, (S_k + kDecodeStepKeys - 1) / kDecodeStepKeys);
@@ -146,10 +163,8 @@ size_t decode_workspace_size(int B, int H_q, int S_k, int D) {
   if (!mul_ok(&n, B) || !mul_ok(&n, H_q) || !mul_ok(&n, max_splits)) return 0;
   int64_t floats = n;
   if (!mul_ok(&floats, (int64_t)D + 1)) return 0;
-  // Partial outputs [B, H_q, splits, D] then partial lse [B, H_q, splits],
-  // the second region starting on a 256-byte boundary.
-  int64_t obytes = ((n * D * 4) + 255) / 256 * 256;
-  return (size_t)(obytes + n * 4);
+  if (floats > ((int64_t)1 << 60) / 4) return 0;
+  return (size_t)decode_layout(B, H_q, (int)max_splits, D).bytes;
 }
 
 int check_decode(const DecodeShape& s, bool* noop) {
@@ -161,6 +176,8 @@ int check_decode(const DecodeShape& s, bool* noop) {
   if (!mul_ok(&nk, s.B) || !mul_ok(&nk, s.S_k) || !mul_ok(&nk, s.H_kv) || !mul_ok(&nk, s.D))
     return fail(SA_ERR_INVALID_ARG, "tensor sizes overflow");
   if (!s.q || !s.out) return fail(SA_ERR_INVALID_ARG, "q and out must not be NULL");
+  if (s.slopes && s.scale == 0.f)
+    return fail(SA_ERR_INVALID_ARG, "scale must be nonzero when ALiBi slopes are given");
   if (s.S_k > 0 && (!s.k || !s.v)) return fail(SA_ERR_INVALID_ARG, "k_cache and v_cache must not be NULL when S_k > 0");
   if (!aligned(s.q, 16) || !aligned(s.out, 16) || (s.k && !aligned(s.k, 16)) || (s.v && !aligned(s.v, 16)))
     return fail(SA_ERR_INVALID_ARG, "q, k_cache, v_cache and out must be 16-byte aligned");

@@ -25,7 +25,10 @@ struct DecodeShape {
 constexpr int kDecodeStepKeys = 128;
 constexpr int kDecodeMaxSplits = 256;
 // Query heads one decode workgroup serves at once (the MFMA column count).
-constexpr int kDecodeHeadGroup = 32;
+constexpr int kDecodeHeadGroup = 16;
+// Keys a decode workgroup addresses per round (4 waves x up to 4 sub-tiles of
+// 32 keys); the last round of a split may run past its end.
+constexpr int kDecodeRoundKeys = 512;
 
 // Records a formatted message as the calling thread's last error and returns
 // the status unchanged.
@@ -48,5 +51,11 @@ int fwd_waves(int B, int S_q, int H_q, bool causal, int num_cu);
 // Keys per split for a split count (a multiple of kDecodeStepKeys).
 int decode_chunk(int S_k, int splits);
 size_t decode_workspace_size(int B, int H_q, int S_k, int D);
+
+// Byte offsets of the decode workspace regions for an actual split count.
+struct DecodeLayout { int64_t o_offset, lse_offset, bytes; };
+DecodeLayout decode_layout(int B, int H_q, int splits, int D);
+// Whether one split's key range can be addressed with 32-bit byte offsets.
+bool decode_offsets_fit(int chunk, int H_kv, int D);
 
 }  // namespace sa

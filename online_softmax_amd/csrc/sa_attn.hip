@@ -65,22 +65,17 @@ void dispatch_fwd(const FwdArgs& args, bool causal, bool mask, bool alibi, int n
   }
 }
 
-template <class T, int D, bool M, bool A>
-void launch_decode(const DecArgs& args, const MergeArgs& margs, int nwg, int nbh, hipStream_t st) {
-  hipLaunchKernelGGL((decode_split_kernel<T, D, M, A>), dim3(nwg), dim3(256), 0, st, args);
-  hipLaunchKernelGGL((decode_merge_kernel<T, D>), dim3(nbh), dim3(256), 0, st, margs);
-}
-
 template <class T, int D>
-void dispatch_decode(const DecArgs& args, const MergeArgs& margs, int nwg, int nbh, bool mask,
-                     bool alibi, hipStream_t st) {
+void dispatch_decode(const DecArgs& args, const MergeArgs& margs, int nwg, bool mask, bool alibi,
+                     hipStream_t st) {
   const int key = (mask ? 2 : 0) | (alibi ? 1 : 0);
   switch (key) {
-    case 0: launch_decode<T, D, false, false>(args, margs, nwg, nbh, st); break;
-    case 1: launch_decode<T, D, false, true>(args, margs, nwg, nbh, st); break;
-    case 2: launch_decode<T, D, true, false>(args, margs, nwg, nbh, st); break;
-    default: launch_decode<T, D, true, true>(args, margs, nwg, nbh, st); break;
+    case 0: hipLaunchKernelGGL((decode_kernel<T, D, false, false>), dim3(nwg), dim3(256), 0, st, args); break;
+    case 1: hipLaunchKernelGGL((decode_kernel<T, D, false, true>), dim3(nwg), dim3(256), 0, st, args); break;
+    case 2: hipLaunchKernelGGL((decode_kernel<T, D, true, false>), dim3(nwg), dim3(256), 0, st, args); break;
+    default: hipLaunchKernelGGL((decode_kernel<T, D, true, true>), dim3(nwg), dim3(256), 0, st, args); break;
   }
+  hipLaunchKernelGGL((decode_merge_kernel<T, D>), dim3(args.B * args.H_q * (D / 16)), dim3(256), 0, st, margs);
 }
 
 }  // namespace
@@ -159,20 +154,26 @@ int sa_attn_decode(const void* q, const void* k_cache, const void* v_cache, void
   const int splits = decode_num_splits(B, S_k, H_q, H_kv, cus);
   const int chunk = decode_chunk(S_k, splits);
   const int64_t nwg = (int64_t)B * H_kv * n_hg * splits;
-  if (nwg > INT32_MAX) return fail(SA_ERR_INVALID_ARG, "too many decode workgroups");
+  if (nwg > INT32_MAX || (int64_t)B * H_q * (D / 16) > INT32_MAX)
+    return fail(SA_ERR_INVALID_ARG, "too many decode workgroups");
+  if (!decode_offsets_fit(chunk, H_kv, D))
+    return fail(SA_ERR_INVALID_ARG, "one decode split would span 4 GiB or more of k_cache");
 
-  const size_t n = (size_t)B * H_q * splits;
+  const DecodeLayout lay = decode_layout(B, H_q, splits, D);
   DecArgs args;
   args.q = (const uint16_t*)q;
   args.k = (const uint16_t*)k_cache;
   args.v = (const uint16_t*)v_cache;
   args.mask = key_padding_mask;
   args.slopes = alibi_slopes;
-  args.ws_o = (float*)workspace;
-  args.ws_lse = (float*)((char*)workspace + (n * D * 4 + 255) / 256 * 256);
+  args.out = (uint16_t*)out;
+  args.lse = lse;
+  args.ws_o = (float*)((char*)workspace + lay.o_offset);
+  args.ws_lse = (float*)((char*)workspace + lay.lse_offset);
   args.B = B; args.S_k = S_k; args.H_q = H_q; args.H_kv = H_kv; args.G = G;
   args.n_hg = n_hg; args.splits = splits; args.chunk = chunk;
   args.scale2 = scale * kLog2e;
+  args.alibi2 = scale != 0.f ? 1.0f / std::fabs(scale) : 0.f;
 
   MergeArgs margs;
   margs.ws_o = args.ws_o;
@@ -182,14 +183,13 @@ int sa_attn_decode(const void* q, const void* k_cache, const void* v_cache, void
   margs.splits = splits;
 
   const bool m = key_padding_mask != nullptr, al = alibi_slopes != nullptr;
-  const int nbh = B * H_q;
   hipStream_t hs = (hipStream_t)stream;
   if (dtype == SA_F16) {
-    if (D == 64) dispatch_decode<F16, 64>(args, margs, (int)nwg, nbh, m, al, hs);
-    else dispatch_decode<F16, 128>(args, margs, (int)nwg, nbh, m, al, hs);
+    if (D == 64) dispatch_decode<F16, 64>(args, margs, (int)nwg, m, al, hs);
+    else dispatch_decode<F16, 128>(args, margs, (int)nwg, m, al, hs);
   } else {
-    if (D == 64) dispatch_decode<BF16, 64>(args, margs, (int)nwg, nbh, m, al, hs);
-    else dispatch_decode<BF16, 128>(args, margs, (int)nwg, nbh, m, al, hs);
+    if (D == 64) dispatch_decode<BF16, 64>(args, margs, (int)nwg, m, al, hs);
+    else dispatch_decode<BF16, 128>(args, margs, (int)nwg, m, al, hs);
   }
   return launched("decode");
 }

@@ -41,7 +41,7 @@ def test_header_symbols_exported(L):
 
 # Fake, 256-byte aligned, non-overlapping addresses (never dereferenced).
 A = 1 << 40
-Q, K, V, O, LSE, WS = (A + i * (1 << 32) for i in range(6))
+Q, K, V, O, LSE, WS, SL = (A + i * (1 << 32) for i in range(7))
 
 
 def fwd(L, q=Q, k=K, v=V, out=O, lse=LSE, B=1, S_q=8, S_k=8, H_q=2, H_kv=2, D=64, scale=0.125,
@@ -75,6 +75,7 @@ def dec(L, q=Q, k=K, v=V, out=O, lse=LSE, B=1, S_k=100, H_q=4, H_kv=2, D=64, sca
     (dict(scale=float("nan")), sa.SA_ERR_INVALID_ARG),
     (dict(out=Q), sa.SA_ERR_INVALID_ARG),          # out aliases q
     (dict(lse=K + 16), sa.SA_ERR_INVALID_ARG),     # lse inside k
+    (dict(slopes=SL, scale=0.0), sa.SA_ERR_INVALID_ARG),  # ALiBi needs a nonzero scale
 ])
 def test_fwd_rejects(L, kw, code):
     assert fwd(L, **kw) == code
@@ -97,6 +98,7 @@ def test_fwd_noop_needs_no_pointers(L):
     (dict(H_q=6, H_kv=4), sa.SA_ERR_INVALID_ARG),
     (dict(ws=K), sa.SA_ERR_INVALID_ARG),           # workspace overlaps k_cache
     (dict(out=WS), sa.SA_ERR_INVALID_ARG),         # out inside the workspace
+    (dict(slopes=SL, scale=0.0), sa.SA_ERR_INVALID_ARG),  # ALiBi needs a nonzero scale
 ])
 def test_decode_rejects(L, kw, code):
     assert dec(L, **kw) == code
@@ -122,8 +124,12 @@ def test_decode_splits_and_workspace(L):
     assert sa.decode_num_splits(1, 1000, 1, 1, 256) == 8
     assert sa.decode_num_splits(1, 10 ** 7, 1, 1, 256) == 256
     assert sa.decode_num_splits(64, 32768, 64, 8, 256) == 1
-    for B, Hq, Hkv, S in [(4, 14, 2, 32768), (1, 40, 1, 300), (3, 8, 8, 1), (2, 6, 3, 129)]:
+    # One (batch, KV head, head group): 256 splits of 128 keys.
+    assert sa.decode_num_splits(1, 32768, 4, 1, 256) == 256
+    for B, Hq, Hkv, S in [(4, 14, 2, 32768), (1, 40, 1, 300), (3, 8, 8, 1), (2, 6, 3, 129),
+                          (1, 4, 1, 32768)]:
         n = sa.decode_num_splits(B, S, Hq, Hkv, 256)
+        # Partial outputs and partial lse of every split.
         need = B * Hq * n * (64 + 1) * 4
         assert sa.decode_workspace_size(B, Hq, S, 64) >= need
     assert sa.decode_workspace_size(-1, 1, 1, 64) == 0

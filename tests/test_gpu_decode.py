@@ -41,6 +41,10 @@ CASES = [
     Workload("dec_k777_all", 2, 1, 777, 28, 4, 128, "bf16", alibi=True, random_tail=300, seed=44),
     Workload("dec_g40_two_groups", 1, 1, 300, 40, 1, 64, "fp16", seed=45),
     Workload("dec_k129_mha", 4, 1, 129, 6, 6, 128, "fp16", seed=46),
+    # One head group, 256 splits of 128 keys: the widest merge.
+    Workload("dec_k32768_256splits", 1, 1, 32768, 4, 1, 128, "bf16", seed=51),
+    # Two full head groups of 16 and 300 keys: rounds past the split's end.
+    Workload("dec_g32_d128", 2, 1, 300, 32, 1, 128, "fp16", alibi=True, seed=52),
 ]
 
 
@@ -91,6 +95,25 @@ def test_decode_workspace_errors():
     with pytest.raises(sa.SaAttnError) as e:
         sa.attn_decode(q, k, v, workspace=small)
     assert e.value.status == sa.SA_ERR_WORKSPACE
+
+
+def test_decode_workspace_reuse():
+    """One workspace serves calls of different sizes in a row."""
+    ws = sa.decode_workspace(3, 32, 40000, 128, "cuda")
+    for i, w in enumerate([Workload("dec_reuse_a", 3, 1, 5000, 14, 2, 64, "fp16", seed=53),
+                           Workload("dec_reuse_b", 1, 1, 40000, 32, 4, 128, "bf16", random_tail=900, seed=54),
+                           Workload("dec_reuse_c", 2, 1, 700, 8, 8, 64, "fp16", alibi=True, seed=55),
+                           Workload("dec_reuse_a", 3, 1, 5000, 14, 2, 64, "fp16", seed=53)]):
+        inp = make_inputs(w)
+        q, k, v, m, s = to_dev(inp)
+        print(f"[decode reuse] call {i}: {w.name}", flush=True)
+        out, lse = sa.attn_decode(q, k, v, scale=w.scale, key_padding_mask=m, alibi_slopes=s,
+                                  workspace=ws)
+        torch.cuda.synchronize()
+        ref_o, ref_l = oracle_for(inp, causal=False)
+        dt = torch.float16 if w.dtype == "fp16" else torch.bfloat16
+        assert_out_close(to_f64(out.cpu()), ref_o, dt, w.name)
+        assert_lse_close(lse.cpu().double().numpy(), ref_l, w.name)
 
 
 def test_decode_deterministic():
