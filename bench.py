@@ -209,7 +209,7 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="c5+c4", choices=sorted(STEPS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--print-source-sha", action="store_true",
