@@ -23,9 +23,14 @@
 //    one exchange between the wave halves, and the probabilities already sit
 //    in the B-operand layout of the next product O^T += V^T P^T;
 //  * V stays row-major in LDS and is read transposed with ds_read_b64_tr_b16;
-//  * software pipeline: iteration t runs S^T of tile t+1 on the matrix cores
-//    while the vector units form the probabilities of tile t, then P·V of
-//    tile t, then prepares tile t+1;
+//  * with ALiBi under the causal rule the workgroup's diagonal band of tiles
+//    is swept first (last tile down), then the tiles from key 0 up: every
+//    wave starts on its own diagonal tile, where the largest biases sit (the
+//    running maximum then settles at once), while the workgroups of a head
+//    still share the tiles from key 0 in L2; otherwise tiles go in key order;
+//  * software pipeline: iteration t runs S^T of the next tile on the matrix
+//    cores while the vector units form the probabilities of tile t, then
+//    P·V of tile t, then prepares the next tile;
 //  * exponentials are base 2 on the hardware exp unit with log2(e) folded into
 //    the score scale; the running maximum lives in that base-2 domain.  The
 //    ALiBi bias (divided by the scale) is the initial value of the S^T
@@ -122,14 +127,25 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_kernel(FwdArgs a) {
     const int rows = min(BN, a.S_k - n0);
     return buffer_rsrc(base + (size_t)n0 * rs, (uint32_t)((rows - 1) * rs * 2 + 2 * D));
   };
+  // Sweep order.  With ALiBi under the causal rule the workgroup's diagonal
+  // band (its last BM / BN tiles) comes first, from the last tile down, and
+  // then the tiles from key 0 upwards: every wave starts on its own diagonal
+  // tile, where the largest biases sit, so the running maximum rarely needs
+  // raising afterwards (in key order it would rise on nearly every tile for
+  // the steeper slopes); and the workgroups of one head still walk the shared
+  // tiles from key 0 together, which keeps them in L2.  Otherwise the order
+  // is plain 0 .. nt-1.
+  constexpr bool BAND = CAUSAL && ALIBI;
+  const int nb = BAND ? min(nt, BM / BN) : 0;
+  auto tile_of = [&](int it) { return it < nb ? nt - 1 - it : it - nb; };
   auto issue_k = [&](int t) {
-    const auto r = tile_rsrc(kb, t * BN);
+    const auto r = tile_rsrc(kb, tile_of(t) * BN);
     uint16_t* buf = Ks[t % NS];
 #pragma unroll
     for (int u = 0; u < NI; ++u) load_lds16(r, buf + (NW * u + w) * 512, voff[u]);
   };
   auto issue_v = [&](int t) {
-    const auto r = tile_rsrc(vb, t * BN);
+    const auto r = tile_rsrc(vb, tile_of(t) * BN);
     uint16_t* buf = Vs[t % NS];
 #pragma unroll
     for (int u = 0; u < NI; ++u) load_lds16(r, buf + (NW * u + w) * 512, voff[u]);
@@ -210,14 +226,14 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_kernel(FwdArgs a) {
       vofs[q][db] = r * D + 8 * ((4 * db + (tr_col >> 3)) ^ lds_swizzle<D>(r)) + (tr_col & 7);
     }
 
-  // Sᵀ = K Qᵀ for the 64 keys of tile t (register r of block jb holds key
-  // n0 + 32 jb + 8 (r/4) + 4 g + r%4).  With ALiBi the accumulator starts at
+  // Sᵀ = K Qᵀ for the 64 keys of the tile of iteration t (register r of
+  // block jb holds key n0 + 32 jb + 8 (r/4) + 4 g + r%4).  With ALiBi the accumulator starts at
   // the bias in accumulator units, -slope |ipos - key| / |scale|; under the
   // causal rule every visible key has key <= ipos, so it is linear there.
   auto qk = [&](const int t, f32x16 (&s)[2]) {
     const uint16_t* kbuf = Ks[t % NS];
     if (ALIBI) {
-      const float rel = (float)(t * BN + 4 * g - ipos);  // key - ipos at r = 0, jb = 0
+      const float rel = (float)(tile_of(t) * BN + 4 * g - ipos);  // key - ipos at r = 0, jb = 0
       const float b0 = slope_acc * rel;
 #pragma unroll
       for (int jb = 0; jb < 2; ++jb)
@@ -247,7 +263,8 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_kernel(FwdArgs a) {
   // and the maximum is taken before scaling.  The reference maximum is raised
   // only when some row's tile maximum exceeds it by more than the slack (rows
   // that need no change get alpha = 1).
-  auto prepare = [&](const int t, f32x16 (&s)[2]) {
+  auto prepare = [&](const int it, f32x16 (&s)[2]) {
+    const int t = tile_of(it);
     const int n0 = t * BN;
     bool masked = n0 + BN > a.S_k || (CAUSAL && n0 + BN - 1 > wrow0 + off);
     bool pad_free = true;
@@ -345,9 +362,14 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_kernel(FwdArgs a) {
   };
 
   // Tiles this wave needs: all of them, or under the causal rule those that
-  // start at or before the wave's furthest visible key.
+  // start at or before the wave's furthest visible key.  They are the
+  // iterations [t0w, t1w): in key order the first ntw, in band-first order
+  // the last ntw (the band tiles past the wave's diagonal come first and are
+  // the ones it skips).
   int ntw = wave_active ? nt : 0;
   if (CAUSAL) ntw = wave_last < 0 ? 0 : min(ntw, wave_last / BN + 1);
+  const int t0w = BAND ? nt - ntw : 0;
+  const int t1w = BAND ? nt : ntw;
 
   // Iteration t issues K of tile t+NS (into the buffer K(t) left, whose Sᵀ
   // was formed in iteration t-1) and V of tile t+NS-1 (into the buffer of
@@ -397,26 +419,39 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_kernel(FwdArgs a) {
   __syncthreads();
 
   f32x16 sa[2], sb[2];
-  if (ntw > 0) {
+  if (ntw > 0 && t0w == 0) {
     qk(0, sa);
     prepare(0, sa);
   }
   // Iteration 0 overwrites the buffer of K(0): every wave must have read it.
   __syncthreads();
   int t = 0;
+  if (BAND) {
+    // Iterations before this wave's first tile take part in the copies and
+    // barriers only.  In the last of them the wave forms Sᵀ of its first
+    // tile: that K landed before the previous barrier, and its buffer is
+    // refilled only after the next one.
+    for (; t < t0w; ++t) {
+      const int n = copies(t);
+      if (ntw > 0 && t + 1 == t0w) {
+        qk(t + 1, sa);
+        prepare(t + 1, sa);
+      }
+      finish(n);
+    }
+  }
   if (ntw > 0) {
-    for (; t + 2 < ntw; t += 2) {
+    for (; t + 2 < t1w; t += 2) {
       full_step(t, sa, sb);
       full_step(t + 1, sb, sa);
     }
-    if (t + 1 < ntw) {
+    if (t + 1 < t1w) {
       full_step(t, sa, sb);
       last_step(t + 1, sb);
-      t += 2;
     } else {
       last_step(t, sa);
-      t += 1;
     }
+    t = t1w;
   }
   // Tiles this wave does not need still take part in the copies and barriers.
   for (; t < nt; ++t) finish(copies(t));

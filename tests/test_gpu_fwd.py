@@ -69,6 +69,11 @@ FEATURES = [
     Workload("s65", 1, 65, 65, 2, 2, 128, "fp16", causal=True, seed=23),
     Workload("s1000", 1, 1000, 1000, 2, 2, 64, "bf16", causal=True, random_tail=300, seed=24),
     Workload("q1_long", 2, 1, 1000, 4, 4, 64, "fp16", seed=25),
+    # Causal ALiBi sweeps each workgroup's diagonal band first: rows with no
+    # visible key (S_q > S_k) and several band tiles with a ragged end.
+    Workload("sq_gt_sk_alibi", 1, 300, 77, 4, 4, 64, "fp16", causal=True, alibi=True, seed=26),
+    Workload("s1000_alibi", 1, 1000, 1000, 2, 2, 64, "fp16", causal=True, alibi=True,
+             random_tail=300, seed=27),
 ]
 
 
