@@ -256,40 +256,45 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_kernel(FwdArgs a) {
     }
   };
 
-  // Visibility and the running-maximum update for tile t.  Keys past the
-  // causal diagonal, past the end of the keys or cleared in the padding mask
-  // are set to -inf in a pass that only tiles touching them take (`masked`
-  // is uniform over the wave).  The scale enters once, in the exponent's fma,
-  // and the maximum is taken before scaling.  The reference maximum is raised
-  // only when some row's tile maximum exceeds it by more than the slack (rows
-  // that need no change get alpha = 1).
-  auto prepare = [&](const int it, f32x16 (&s)[2]) {
+  // Visibility and the running-maximum update for the tile of iteration it.
+  // Keys past the causal diagonal, past the end of the keys or cleared in the
+  // padding mask are set to -inf in a pass that only tiles touching them take
+  // (`tile_masked` is uniform over the wave).  The scale enters once, in the
+  // exponent's fma, and the maximum is taken before scaling.  The reference
+  // maximum is raised only when some row's tile maximum exceeds it by more
+  // than the slack (rows that need no change get alpha = 1).
+  auto tile_masked = [&](const int it) -> bool {
     const int t = tile_of(it);
     const int n0 = t * BN;
     bool masked = n0 + BN > a.S_k || (CAUSAL && n0 + BN - 1 > wrow0 + off);
-    bool pad_free = true;
-    if (MASK) {
-      pad_free = t < kMaskFlagTiles && ((Mf[t >> 5] >> (t & 31)) & 1u);
-      masked = masked || !pad_free;
-    }
-    if (masked) {
-#pragma unroll
-      for (int jb = 0; jb < 2; ++jb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int kj = n0 + 4 * g + 32 * jb + 8 * (r >> 2) + (r & 3);
-          bool vis = kj < a.S_k;
-          if (CAUSAL) vis = vis && kj <= ipos;
-          if (MASK && !pad_free) vis = vis && mrow[vis ? kj : 0] != 0;
-          s[jb][r] = vis ? s[jb][r] : kNegInf;
-        }
-    }
-    float tmax = kNegInf;
+    if (MASK) masked = masked || !(t < kMaskFlagTiles && ((Mf[t >> 5] >> (t & 31)) & 1u));
+    return masked;
+  };
+  auto mask_tile = [&](const int it, f32x16 (&s)[2]) {
+    const int t = tile_of(it);
+    const int n0 = t * BN;
+    const bool pad_free = !MASK || (t < kMaskFlagTiles && ((Mf[t >> 5] >> (t & 31)) & 1u));
 #pragma unroll
     for (int jb = 0; jb < 2; ++jb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) tmax = fmaxf(tmax, s[jb][r]);
-    tmax = max_halves(tmax) * sc2;
+      for (int r = 0; r < 16; ++r) {
+        const int kj = n0 + 4 * g + 32 * jb + 8 * (r >> 2) + (r & 3);
+        bool vis = kj < a.S_k;
+        if (CAUSAL) vis = vis && kj <= ipos;
+        if (MASK && !pad_free) vis = vis && mrow[vis ? kj : 0] != 0;
+        s[jb][r] = vis ? s[jb][r] : kNegInf;
+      }
+  };
+  // Row maximum of a tile in the base-2 domain (same value in both halves).
+  auto tile_max = [&](const f32x16 (&s)[2]) -> float {
+    float mx[2] = {kNegInf, kNegInf};  // two independent chains
+#pragma unroll
+    for (int jb = 0; jb < 2; ++jb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx[jb] = fmaxf(mx[jb], s[jb][r]);
+    return max_halves(fmaxf(mx[0], mx[1])) * sc2;
+  };
+  auto raise_max = [&](const float tmax) {
     if (wave_any(tmax > m_ref + kRescaleSlack)) {
       const float m_new = fmaxf(m_ref, tmax);
       const float alpha = m_new == kNegInf ? 1.f : fast_exp2(m_ref - m_new);
@@ -299,24 +304,28 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_kernel(FwdArgs a) {
       for (int db = 0; db < DB; ++db) o[db] *= alpha;
     }
   };
+  auto prepare = [&](const int it, f32x16 (&s)[2]) {
+    if (tile_masked(it)) mask_tile(it, s);
+    raise_max(tile_max(s));
+  };
 
   // Probabilities of a prepared tile, packed to the input type, and their sum.
   // While a row has seen no visible key its reference is 0, so that no
   // exp(-inf - (-inf)) is formed.
   auto softmax_exp = [&](const f32x16 (&s)[2], uint32_t (&pk)[2][8]) {
     const float nm = m_ref == kNegInf ? 0.f : -m_ref;
-    float psum = 0.f;
+    float ps[2] = {0.f, 0.f};  // two partial sums: shorter dependency chains
 #pragma unroll
     for (int jb = 0; jb < 2; ++jb) {
 #pragma unroll
       for (int r = 0; r < 16; r += 2) {
         const float p0 = fast_exp2(fmaf(s[jb][r], sc2, nm));
         const float p1 = fast_exp2(fmaf(s[jb][r + 1], sc2, nm));
-        psum += p0 + p1;
+        ps[jb] += p0 + p1;
         pk[jb][r >> 1] = T::pack2(p0, p1);
       }
     }
-    l_run += psum;
+    l_run += ps[0] + ps[1];
   };
 
   // Oᵀ += Vᵀ Pᵀ over four 16-key steps of tile t.
@@ -338,10 +347,10 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_kernel(FwdArgs a) {
   };
 
   // Instruction order for the block {Sᵀ of tile t+1, exponentials of tile t,
-  // P·V of tile t}: keep a few K reads ahead of the Sᵀ MFMAs and put the
-  // exponential work between them, so that neither the LDS latency nor the
-  // vector work leaves the matrix cores idle; then P·V with its transposed
-  // V reads two ahead.
+  // P·V of tile t, maximum of tile t+1}: keep a few K reads ahead of the Sᵀ
+  // MFMAs and put the exponential work between them, so that neither the LDS
+  // latency nor the vector work leaves the matrix cores idle; then P·V with
+  // its transposed V reads three MFMAs ahead and the maximum between them.
   auto interleave_schedule = [&]() {
     constexpr int kMfma = 0x008, kValu = 0x002 | 0x400, kDsRead = 0x100;
     constexpr int NQK = 2 * KK, NPV = 4 * DB;
@@ -352,12 +361,12 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_kernel(FwdArgs a) {
       __builtin_amdgcn_sched_group_barrier(kValu, 5, 0);
       if (i + 4 < NQK) __builtin_amdgcn_sched_group_barrier(kDsRead, 1, 0);
     }
-    __builtin_amdgcn_sched_group_barrier(kDsRead, 4, 0);
+    __builtin_amdgcn_sched_group_barrier(kDsRead, 6, 0);
 #pragma unroll
     for (int i = 0; i < NPV; ++i) {
       __builtin_amdgcn_sched_group_barrier(kMfma, 1, 0);
-      if (i + 2 < NPV) __builtin_amdgcn_sched_group_barrier(kDsRead, 2, 0);
-      __builtin_amdgcn_sched_group_barrier(kValu, 2, 0);
+      if (i + 3 < NPV) __builtin_amdgcn_sched_group_barrier(kDsRead, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(kValu, 4, 0);
     }
   };
 
@@ -396,14 +405,25 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_kernel(FwdArgs a) {
   };
   // A full step: Sᵀ of tile t+1, probabilities and P·V of tile t, then the
   // preparation of tile t+1.
+  // The maximum of tile t+1 is first taken as if no key were hidden, in the
+  // same block as the matrix work (every score is finite); a tile that has
+  // hidden keys masks them and takes it again.
   auto full_step = [&](const int t, f32x16 (&s)[2], f32x16 (&sn)[2]) {
     const int n = copies(t);
     uint32_t pk[2][8];
     qk(t + 1, sn);
     softmax_exp(s, pk);
     pv(t, pk);
+    float tmax = tile_max(sn);
     interleave_schedule();
-    prepare(t + 1, sn);
+    // Keep the row sum in this block, where the matrix work hides it (the
+    // compiler would otherwise sink it past the masking branch).
+    __asm__ volatile("" : "+v"(l_run));
+    if (tile_masked(t + 1)) {
+      mask_tile(t + 1, sn);
+      tmax = tile_max(sn);
+    }
+    raise_max(tmax);
     finish(n);
   };
   // The wave's last tile: probabilities and P·V only.
