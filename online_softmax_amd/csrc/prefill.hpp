@@ -230,30 +230,30 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_kernel(FwdArgs a) {
   // block jb holds key n0 + 32 jb + 8 (r/4) + 4 g + r%4).  With ALiBi the accumulator starts at
   // the bias in accumulator units, -slope |ipos - key| / |scale|; under the
   // causal rule every visible key has key <= ipos, so it is linear there.
-  auto qk = [&](const int t, f32x16 (&s)[2]) {
-    const uint16_t* kbuf = Ks[t % NS];
+  auto init_scores = [&](const int t, const int jb, f32x16 (&s)[2]) {
     if (ALIBI) {
       const float rel = (float)(tile_of(t) * BN + 4 * g - ipos);  // key - ipos at r = 0, jb = 0
       const float b0 = slope_acc * rel;
 #pragma unroll
-      for (int jb = 0; jb < 2; ++jb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float kofs = (float)(32 * jb + 8 * (r >> 2) + (r & 3));
-          s[jb][r] = CAUSAL ? fmaf(slope_acc, kofs, b0) : -slope_acc * __builtin_fabsf(rel + kofs);
-        }
-    } else {
-      s[0] = (f32x16){};
-      s[1] = (f32x16){};
-    }
-#pragma unroll
-    for (int kk = 0; kk < KK; ++kk) {
-#pragma unroll
-      for (int jb = 0; jb < 2; ++jb) {
-        const u32x4 ak = *(const u32x4*)&kbuf[(32 * jb + li) * D + 8 * ((2 * kk + g) ^ ksw)];
-        s[jb] = T::mma(ak, qreg[kk], s[jb]);
+      for (int r = 0; r < 16; ++r) {
+        const float kofs = (float)(32 * jb + 8 * (r >> 2) + (r & 3));
+        s[jb][r] = CAUSAL ? fmaf(slope_acc, kofs, b0) : -slope_acc * __builtin_fabsf(rel + kofs);
       }
+    } else {
+      s[jb] = (f32x16){};
     }
+  };
+  // K fragment of Sᵀ MFMA i (k-step i/2, key block i%2).
+  auto k_frag = [&](const uint16_t* kbuf, const int i) -> u32x4 {
+    const int kk = i >> 1, jb = i & 1;
+    return *(const u32x4*)&kbuf[(32 * jb + li) * D + 8 * ((2 * kk + g) ^ ksw)];
+  };
+  auto qk = [&](const int t, f32x16 (&s)[2]) {
+    const uint16_t* kbuf = Ks[t % NS];
+    init_scores(t, 0, s);
+    init_scores(t, 1, s);
+#pragma unroll
+    for (int i = 0; i < 2 * KK; ++i) s[i & 1] = T::mma(k_frag(kbuf, i), qreg[i >> 1], s[i & 1]);
   };
 
   // Visibility and the running-maximum update for the tile of iteration it.
@@ -370,6 +370,89 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_kernel(FwdArgs a) {
     }
   };
 
+  // The two phases of a pipelined step, each in a fixed instruction order
+  // (a scheduling barrier closes every chunk): left free, the scheduler
+  // either bunched the vector work behind the matrix work or, with ALiBi,
+  // started P·V before Sᵀ and left the exponentials exposed.  The sixteen
+  // pairs of exponentials of the current tile are split between the phases:
+  // the first EQ under the Sᵀ MFMAs of the next tile, the rest under the
+  // first P·V MFMAs (those that use only the first EQ pairs).
+  constexpr int NQK = 2 * KK, NPV = 4 * DB, EQ = 8;
+  // P·V MFMAs 0 .. NPV/2-1 use only pairs 0 .. 7 (keys 0 .. 31 of the tile).
+  static_assert(EQ >= 8 && EQ <= 16, "pair split");
+  // One pair of probabilities: exponentials, packed to the input type, summed.
+  auto exp_pair = [&](const f32x16 (&s)[2], const int pi, const float nm, uint32_t (&pk)[2][8],
+                      float (&ps)[2]) {
+    const int jb = pi >> 3, r = 2 * (pi & 7);
+    const float p0 = fast_exp2(fmaf(s[jb][r], sc2, nm));
+    const float p1 = fast_exp2(fmaf(s[jb][r + 1], sc2, nm));
+    ps[jb] += p0 + p1;
+    pk[jb][r >> 1] = T::pack2(p0, p1);
+  };
+  // Phase 1: Sᵀ of the tile of iteration t1 (K fragments read four MFMAs
+  // ahead) with pairs 0 .. EQ-1 of the current tile s.
+  auto qk_exp = [&](const int t1, f32x16 (&sn)[2], const f32x16 (&s)[2], const float nm,
+                    uint32_t (&pk)[2][8], float (&ps)[2]) {
+    const uint16_t* kbuf = Ks[t1 % NS];
+    u32x4 ak[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) ak[i] = k_frag(kbuf, i);
+    init_scores(t1, 0, sn);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int i = 0; i < NQK; ++i) {
+      sn[i & 1] = T::mma(ak[i & 3], qreg[i >> 1], sn[i & 1]);
+      if (i + 4 < NQK) ak[i & 3] = k_frag(kbuf, i + 4);
+      if (i == 0) init_scores(t1, 1, sn);
+#pragma unroll
+      for (int pi = i * EQ / NQK; pi < (i + 1) * EQ / NQK; ++pi) exp_pair(s, pi, nm, pk, ps);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+  // Phase 2: Oᵀ += Vᵀ Pᵀ for the tile of iteration t (transposed V reads three
+  // MFMAs ahead) with pairs EQ .. 15 under its first MFMAs, and the row
+  // maximum of the next tile sn (as if no key were hidden) in two chains.
+  auto pv_max = [&](const int t, const f32x16 (&s)[2], const float nm, uint32_t (&pk)[2][8],
+                    float (&ps)[2], const f32x16 (&sn)[2]) -> float {
+    const uint16_t* vbuf = Vs[t % NS];
+    auto v_frag = [&](const int i) -> u32x4 {
+      const int ks = i / DB, db = i % DB;
+      const uint16_t* vt = vbuf + 16 * ks * D;
+      const u32x2 lo = lds_read_tr(vt + vofs[0][db]);
+      const u32x2 hi = lds_read_tr(vt + vofs[1][db]);
+      return (u32x4){lo[0], lo[1], hi[0], hi[1]};
+    };
+    u32x4 av[3];
+#pragma unroll
+    for (int i = 0; i < 3; ++i) av[i] = v_frag(i);
+    float mx[2] = {kNegInf, kNegInf};
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int i = 0; i < NPV; ++i) {
+      const int ks = i / DB, db = i % DB, jb = ks >> 1, mh = ks & 1;
+      const u32x4 bp = {pk[jb][4 * mh], pk[jb][4 * mh + 1], pk[jb][4 * mh + 2], pk[jb][4 * mh + 3]};
+      o[db] = T::mma(av[i % 3], bp, o[db]);
+      if (i + 3 < NPV) av[i % 3] = v_frag(i + 3);
+      constexpr int H = NPV / 2;
+      if (i < H) {
+#pragma unroll
+        for (int pi = EQ + i * (16 - EQ) / H; pi < EQ + (i + 1) * (16 - EQ) / H; ++pi)
+          exp_pair(s, pi, nm, pk, ps);
+      }
+#pragma unroll
+      for (int e = 0; e < 32 / NPV; e += 2) {
+        const int vi = i * (32 / NPV) + e;  // score 0..31
+        const int sj = vi >> 4, r = vi & 15;
+        mx[sj] = fmaxf(fmaxf(mx[sj], sn[sj][r]), sn[sj][r + 1]);
+      }
+      // Pin this step of the maximum here (it depends on nothing in the loop
+      // and would otherwise be sunk past it).
+      __asm__ volatile("" : "+v"(mx[0]), "+v"(mx[1]));
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    return max_halves(fmaxf(mx[0], mx[1])) * sc2;
+  };
+
   // Tiles this wave needs: all of them, or under the causal rule those that
   // start at or before the wave's furthest visible key.  They are the
   // iterations [t0w, t1w): in key order the first ntw, in band-first order
@@ -405,20 +488,31 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_kernel(FwdArgs a) {
   };
   // A full step: Sᵀ of tile t+1, probabilities and P·V of tile t, then the
   // preparation of tile t+1.
-  // The maximum of tile t+1 is first taken as if no key were hidden, in the
-  // same block as the matrix work (every score is finite); a tile that has
-  // hidden keys masks them and takes it again.
+  // The maximum of tile t+1 is first taken as if no key were hidden, during
+  // the matrix work (every score is finite); a tile that has hidden keys
+  // masks them and takes it again.  With ALiBi the step runs in the fixed
+  // order above; otherwise the scheduler places the same work after the
+  // pattern of interleave_schedule, which measured faster there.
   auto full_step = [&](const int t, f32x16 (&s)[2], f32x16 (&sn)[2]) {
     const int n = copies(t);
     uint32_t pk[2][8];
-    qk(t + 1, sn);
-    softmax_exp(s, pk);
-    pv(t, pk);
-    float tmax = tile_max(sn);
-    interleave_schedule();
-    // Keep the row sum in this block, where the matrix work hides it (the
-    // compiler would otherwise sink it past the masking branch).
-    __asm__ volatile("" : "+v"(l_run));
+    float tmax;
+    if constexpr (ALIBI) {
+      float ps[2] = {0.f, 0.f};
+      const float nm = m_ref == kNegInf ? 0.f : -m_ref;
+      qk_exp(t + 1, sn, s, nm, pk, ps);
+      tmax = pv_max(t, s, nm, pk, ps, sn);
+      l_run += ps[0] + ps[1];
+    } else {
+      qk(t + 1, sn);
+      softmax_exp(s, pk);
+      pv(t, pk);
+      tmax = tile_max(sn);
+      interleave_schedule();
+      // Keep the row sum in this block, where the matrix work hides it (the
+      // compiler would otherwise sink it past the masking branch).
+      __asm__ volatile("" : "+v"(l_run));
+    }
     if (tile_masked(t + 1)) {
       mask_tile(t + 1, sn);
       tmax = tile_max(sn);
