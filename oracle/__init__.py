@@ -14,6 +14,9 @@ fast:
 * ``online_attention`` — the pages' streaming recurrence (running max, rescaled
   numerator and denominator, one key block at a time) in float64, kept to show
   that the recurrence reaches the definition.
+* ``attention_bwd`` — the gradients dq, dk, dv of the attention output by
+  their definition (the single-sweep backward of the "StreamAttention" page,
+  "Recent Updates"; "flash-attn-volta" page, "Backward correctness").
 * ``merge_states`` — the log-sum-exp weighted combination of partial states
   ("StreamAttention" page, "Engine Direction" and "Distributed and
   Long-Context Variants").
@@ -23,9 +26,9 @@ Every function here is pinned by tests that do not go through the oracle's own
 code path (closed forms, invariants, a library routine, brute force); none of
 them is "parity unpinned".
 """
-from .attention import (attention, attention_probs, online_attention,
+from .attention import (attention, attention_bwd, attention_probs, online_attention,
                         merge_states, partial_state, alibi_bias, visible)
 from . import brute
 
-__all__ = ["attention", "attention_probs", "online_attention", "merge_states",
+__all__ = ["attention", "attention_bwd", "attention_probs", "online_attention", "merge_states",
            "partial_state", "alibi_bias", "visible", "brute"]

@@ -226,3 +226,59 @@ def merge_states(o_parts, lse_parts):
         wn = np.where(tot[None] > 0, w / tot[None], 0.0)
     out = (wn[..., None] * o_parts).sum(axis=0)
     return out, lse
+
+
+def attention_bwd(q, k, v, dout, scale, causal=False, key_padding_mask=None,
+                  alibi_slopes=None):
+    """Gradients of the attention output by its definition, in float64.
+
+    The single-sweep backward of the "StreamAttention: Fused Online Softmax
+    Attention" page ("Recent Updates", "Backward": recompute the score tiles
+    from the saved lse and stream dQ, dK and dV) and of the "flash-attn-volta"
+    page ("Backward correctness") computes these same quantities.  With
+    ``P = softmax(s)`` over the visible keys of each row and ``out = P v``:
+
+    * ``dv_j  = sum_i P[i, j] dout_i``
+    * ``dP[i, j] = <dout_i, v_j>``
+    * ``Di    = sum_j P[i, j] dP[i, j]  ( = <dout_i, out_i> )``
+    * ``dS[i, j] = P[i, j] (dP[i, j] - Di)``
+    * ``dq_i  = scale * sum_j dS[i, j] k_j``,  ``dk_j = scale * sum_i dS[i, j] q_i``
+
+    Hidden keys have ``P = 0`` and get no gradient from that row; the bias
+    and the mask carry no gradient.  A key/value head receives the sum over
+    the query heads that read it.  Returns ``dq [B, S_q, H_q, D]``,
+    ``dk, dv [B, S_k, H_kv, D]``.
+    """
+    q, k, v, dout = _f64(q), _f64(k), _f64(v), _f64(dout)
+    B, S_q, H_q, D = q.shape
+    S_k, H_kv = k.shape[1], k.shape[2]
+    if H_q % H_kv:
+        raise ValueError("H_q must be a multiple of H_kv")
+    G = H_q // H_kv
+    dq = np.zeros_like(q)
+    dk = np.zeros_like(k)
+    dv = np.zeros_like(v)
+    for b in range(B):
+        mrow = None if key_padding_mask is None else np.asarray(key_padding_mask)[b]
+        keep = visible(S_q, S_k, causal, mrow)
+        for h in range(H_q):
+            hk = h // G
+            bias = None
+            if alibi_slopes is not None:
+                bias = alibi_bias(np.asarray(alibi_slopes, np.float64)[h], S_q, S_k)
+            P, _ = _softmax_rows(_scores(q[b, :, h, :], k[b, :, hk, :], scale, keep, bias))
+            dqh, dkh, dvh = _bwd_head(P, dout[b, :, h, :], q[b, :, h, :], k[b, :, hk, :],
+                                      v[b, :, hk, :], float(scale))
+            dq[b, :, h, :] = dqh
+            dk[b, :, hk, :] += dkh
+            dv[b, :, hk, :] += dvh
+    return dq, dk, dv
+
+
+def _bwd_head(P, do, qh, kh, vh, scale):
+    """Gradients of one (batch, query head) from its probabilities ``P``."""
+    dv = P.T @ do
+    dP = do @ vh.T
+    Di = (P * dP).sum(axis=1)
+    dS = P * (dP - Di[:, None])
+    return scale * (dS @ kh), scale * (dS.T @ qh), dv

@@ -24,7 +24,10 @@ import pytest
 import torch
 
 import oracle
-import oracle.attention as oatt
+import importlib
+
+# The module itself: the package re-exports a function under the same name.
+oatt = importlib.import_module("oracle.attention")
 from workloads import WORKLOADS, Workload, alibi_slopes, make_inputs, to_f64
 
 GOLDEN = Path(__file__).parent / "golden" / "worked_examples.json"
@@ -377,6 +380,23 @@ def _interleave(H_q, H_kv):
     """Head order that maps query head h to KV head h % H_kv instead of h // G."""
     G = H_q // H_kv
     return np.array([(h % H_kv) * G for h in range(H_q)])
+
+
+@pytest.mark.parametrize("name", list(MUTANTS))
+def test_mutants_run_and_differ(name):
+    """Each planted mistake runs and changes the result on a generic input
+    (so that its rejection below is not an artefact of the test machinery)."""
+    rng = np.random.default_rng(77)
+    q, k, v = rnd(rng, 2, 6, 4, 3), rnd(rng, 2, 8, 2, 3), rnd(rng, 2, 8, 2, 3)
+    mask = np.ones((2, 8), np.uint8)
+    mask[0, 5] = 0
+    differs = False
+    for causal in (True, False):   # some mistakes only show without the causal rule
+        args = (q, k, v, 0.7, causal, mask, np.array([0.5, 0.25, 0.125, 0.0625]))
+        got = MUTANTS[name](*args)
+        ref = call_oracle(*args)
+        differs = differs or not (close(got[0], ref[0], 1e-9) and close(got[1], ref[1], 1e-9))
+    assert differs
 
 
 @pytest.mark.parametrize("name", list(MUTANTS))
