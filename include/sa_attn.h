@@ -129,6 +129,46 @@ int sa_attn_decode(const void* q, const void* k_cache, const void* v_cache,
  * num_cu compute units (host arithmetic only; exposed for tests and tools). */
 int sa_attn_decode_num_splits(int B, int S_k, int H_q, int H_kv, int num_cu);
 
+/*
+ * Bytes of device workspace sa_attn_bwd needs: one float2 per (batch, query
+ * head, row), B * H_q * S_q * 8.  Pure host arithmetic; 0 for a negative
+ * size or on overflow.
+ */
+size_t sa_attn_bwd_workspace_size(int B, int H_q, int S_q);
+
+/*
+ * Gradients of sa_attn_fwd's output: the single-sweep backward of the
+ * "StreamAttention" page ("Recent Updates": recompute the score tiles from
+ * the saved lse, stream dQ, dK and dV) and the quantities the
+ * "flash-attn-volta" page checks ("Backward correctness").  With P the
+ * attention probabilities over the visible keys (same causal rule, mask and
+ * ALiBi bias as the forward, neither of which has a gradient):
+ *   dv = P^T dout,  dS = P (dout V^T - rowsum(dout * out)),
+ *   dq = scale dS K,  dk = scale dS^T q,
+ * each KV head receiving the sum over the query heads that read it.
+ *
+ *   q, out, dout  [B, S_q, H_q, D]   dtype, device (out: the forward's output)
+ *   k, v          [B, S_k, H_kv, D]  dtype, device
+ *   lse           [B, H_q, S_q]      float32, device: the forward's lse
+ *   dq            [B, S_q, H_q, D]   dtype, device, fully written
+ *   dk, dv        [B, S_k, H_kv, D]  dtype, device, fully written
+ *   other arguments as for sa_attn_fwd
+ *   workspace, workspace_bytes: caller-owned device scratch of at least
+ *     sa_attn_bwd_workspace_size(B, H_q, S_q) bytes, 16-byte aligned, when
+ *     S_q > 0; contents on entry do not matter.
+ *
+ * The gradients accumulate in float32 in a fixed order (no atomics): the
+ * same inputs give bit-identical outputs.  B == 0, or S_q == S_k == 0, is a
+ * no-op; S_q == 0 writes dk = dv = 0 and S_k == 0 writes dq = 0.  Errors as
+ * for sa_attn_fwd, plus SA_ERR_WORKSPACE; outputs must not overlap inputs,
+ * each other or the workspace.
+ */
+int sa_attn_bwd(const void* q, const void* k, const void* v, const void* out, const void* dout,
+                const float* lse, void* dq, void* dk, void* dv, int B, int S_q, int S_k, int H_q,
+                int H_kv, int D, float scale, int causal, const uint8_t* key_padding_mask,
+                const float* alibi_slopes, int dtype, void* workspace, size_t workspace_bytes,
+                sa_stream_t stream);
+
 /* Static description of a status code. */
 const char* sa_status_string(int status);
 

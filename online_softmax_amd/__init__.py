@@ -14,6 +14,8 @@ Functions keep the names of the C entry points:
 * ``attn_decode(q, k_cache, v_cache, scale=None, key_padding_mask=None,
   alibi_slopes=None, out=None, lse=None, workspace=None, return_lse=True)``
 * ``decode_workspace_size(B, H_q, S_k, D)`` and ``decode_num_splits(...)``
+* ``attn_bwd(q, k, v, out, dout, lse, causal=False, scale=None, key_padding_mask=None,
+  alibi_slopes=None)`` -> ``(dq, dk, dv)`` and ``bwd_workspace_size(B, H_q, S_q)``
 """
 from __future__ import annotations
 
@@ -38,6 +40,9 @@ SIGNATURES = {
     "sa_attn_decode_workspace_size": (_SZ, [_I, _I, _I, _I]),
     "sa_attn_decode": (_I, [_VP, _VP, _VP, _VP, _FP, _I, _I, _I, _I, _I, _F, _U8P, _FP, _I, _VP, _SZ, _VP]),
     "sa_attn_decode_num_splits": (_I, [_I, _I, _I, _I, _I]),
+    "sa_attn_bwd_workspace_size": (_SZ, [_I, _I, _I]),
+    "sa_attn_bwd": (_I, [_VP, _VP, _VP, _VP, _VP, _FP, _VP, _VP, _VP, _I, _I, _I, _I, _I, _I, _F,
+                         _I, _U8P, _FP, _I, _VP, _SZ, _VP]),
     "sa_status_string": (ctypes.c_char_p, [_I]),
     "sa_last_error": (ctypes.c_char_p, []),
 }
@@ -212,7 +217,57 @@ def attn_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
     return (out, lse) if return_lse else out
 
 
-__all__ = ["attn_fwd", "attn_decode", "decode_workspace_size", "decode_num_splits",
+def bwd_workspace_size(B: int, H_q: int, S_q: int) -> int:
+    return int(lib().sa_attn_bwd_workspace_size(B, H_q, S_q))
+
+
+def attn_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torch.Tensor,
+             dout: torch.Tensor, lse: torch.Tensor, causal: bool = False,
+             scale: Optional[float] = None, key_padding_mask: Optional[torch.Tensor] = None,
+             alibi_slopes: Optional[torch.Tensor] = None, dq: Optional[torch.Tensor] = None,
+             dk: Optional[torch.Tensor] = None, dv: Optional[torch.Tensor] = None,
+             workspace: Optional[torch.Tensor] = None):
+    """Gradients of ``attn_fwd``'s output through ``sa_attn_bwd``.
+
+    ``out`` and ``lse`` are what ``attn_fwd`` returned for the same inputs;
+    ``dout`` has the shape of ``out``.  Returns ``(dq, dk, dv)``.
+    """
+    _need(q, "q")
+    if q.dtype not in _DTYPE:
+        raise ValueError(f"unsupported dtype {q.dtype}")
+    dev = q.device
+    B, S_q, H_q, D = q.shape
+    _need(k, "k", q.dtype, None, dev)
+    if k.dim() != 4 or k.shape[0] != B or k.shape[3] != D:
+        raise ValueError(f"k has shape {tuple(k.shape)}, incompatible with q {tuple(q.shape)}")
+    S_k, H_kv = k.shape[1], k.shape[2]
+    _need(v, "v", q.dtype, k.shape, dev)
+    _need(out, "out", q.dtype, q.shape, dev)
+    _need(dout, "dout", q.dtype, q.shape, dev)
+    _need(lse, "lse", torch.float32, (B, H_q, S_q), dev)
+    mask = _mask_arg(key_padding_mask, B, S_k, dev)
+    if alibi_slopes is not None:
+        _need(alibi_slopes, "alibi_slopes", torch.float32, (H_q,), dev)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    _need(dq, "dq", q.dtype, q.shape, dev)
+    _need(dk, "dk", q.dtype, k.shape, dev)
+    _need(dv, "dv", q.dtype, k.shape, dev)
+    if workspace is None:
+        workspace = torch.empty(max(bwd_workspace_size(B, H_q, S_q), 16), dtype=torch.uint8, device=dev)
+    _need(workspace, "workspace", None, None, dev)
+    sc = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    st = lib().sa_attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(dout), _ptr(lse),
+                           _ptr(dq), _ptr(dk), _ptr(dv), B, S_q, S_k, H_q, H_kv, D, sc,
+                           int(bool(causal)), _ptr(mask), _ptr(alibi_slopes), _DTYPE[q.dtype],
+                           workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+                           _stream(dev))
+    _check(st)
+    return dq, dk, dv
+
+
+__all__ = ["attn_fwd", "attn_decode", "attn_bwd", "bwd_workspace_size", "decode_workspace_size", "decode_num_splits",
            "decode_workspace", "lib", "last_error", "status_string", "SaAttnError",
            "SIGNATURES", "LIB_PATH", "SA_OK", "SA_ERR_INVALID_ARG", "SA_ERR_UNSUPPORTED",
            "SA_ERR_WORKSPACE", "SA_ERR_HIP", "SA_F16", "SA_BF16"]

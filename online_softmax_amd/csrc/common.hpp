@@ -40,6 +40,10 @@ struct F16 {
     f32x2 v = {lo, hi};
     return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, f16x2));
   }
+  // A packed pair to two floats (exact).
+  __device__ static inline f32x2 unpack2(uint32_t x) {
+    return __builtin_convertvector(__builtin_bit_cast(f16x2, x), f32x2);
+  }
 };
 
 struct BF16 {
@@ -54,6 +58,10 @@ struct BF16 {
   __device__ static inline uint32_t pack2(float lo, float hi) {
     f32x2 v = {lo, hi};
     return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
+  }
+  // bf16 is the upper half of a float.
+  __device__ static inline f32x2 unpack2(uint32_t x) {
+    return (f32x2){__uint_as_float(x << 16), __uint_as_float(x & 0xffff0000u)};
   }
 };
 

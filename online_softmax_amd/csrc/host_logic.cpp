@@ -204,4 +204,66 @@ int check_decode(const DecodeShape& s, bool* noop) {
   return SA_OK;
 }
 
+size_t bwd_workspace_size(int B, int H_q, int S_q) {
+  if (B < 0 || H_q < 0 || S_q < 0) return 0;
+  int64_t n = 8;
+  if (!mul_ok(&n, B) || !mul_ok(&n, H_q) || !mul_ok(&n, S_q)) return 0;
+  return (size_t)n;
+}
+
+int check_bwd(const BwdShape& s, bool* noop) {
+  *noop = false;
+  int st = check_common(s.dtype, s.D, s.B, s.S_k, s.H_q, s.H_kv, s.scale);
+  if (st != SA_OK) return st;
+  if (s.S_q < 0) return fail(SA_ERR_INVALID_ARG, "negative S_q=%d", s.S_q);
+  if (s.causal != 0 && s.causal != 1) return fail(SA_ERR_INVALID_ARG, "causal must be 0 or 1");
+  if (s.slopes && s.scale == 0.f)
+    return fail(SA_ERR_INVALID_ARG, "scale must be nonzero when ALiBi slopes are given");
+  // With no query rows dk and dv are zero; with no keys dq is zero: both are
+  // still written.  Only an empty batch, or no rows and no keys, is a no-op.
+  if (s.B == 0 || (s.S_q == 0 && s.S_k == 0)) { *noop = true; return SA_OK; }
+  int64_t nq = 1, nk = 1;
+  if (!mul_ok(&nq, s.B) || !mul_ok(&nq, s.S_q) || !mul_ok(&nq, s.H_q) || !mul_ok(&nq, s.D) ||
+      !mul_ok(&nk, s.B) || !mul_ok(&nk, s.S_k) || !mul_ok(&nk, s.H_kv) || !mul_ok(&nk, s.D))
+    return fail(SA_ERR_INVALID_ARG, "tensor sizes overflow");
+  // Grids (1-D) and 32-bit buffer ranges of the tile copies.
+  if ((int64_t)s.B * s.H_q * ((s.S_q + 127) / 128) > INT32_MAX ||
+      (int64_t)s.B * s.H_kv * ((s.S_k + 127) / 128) > INT32_MAX ||
+      ((int64_t)s.B * s.H_q * s.S_q + 255) / 256 > INT32_MAX)
+    return fail(SA_ERR_INVALID_ARG, "too many rows or keys for the launch grids");
+  if ((int64_t)64 * s.H_kv * s.D * 2 >= (INT64_C(1) << 32) || (int64_t)32 * s.H_q * s.D * 2 >= (INT64_C(1) << 32))
+    return fail(SA_ERR_UNSUPPORTED, "H * D too large for the tile copies");
+  const bool rows = s.S_q > 0, keys = s.S_k > 0;
+  if (rows && (!s.q || !s.out || !s.dout || !s.lse || !s.dq))
+    return fail(SA_ERR_INVALID_ARG, "q, out, dout, lse and dq must not be NULL when S_q > 0");
+  if (keys && (!s.k || !s.v || !s.dk || !s.dv))
+    return fail(SA_ERR_INVALID_ARG, "k, v, dk and dv must not be NULL when S_k > 0");
+  const void* a16[8] = {s.q, s.k, s.v, s.out, s.dout, s.dq, s.dk, s.dv};
+  for (const void* p : a16)
+    if (p && !aligned(p, 16)) return fail(SA_ERR_INVALID_ARG, "q, k, v, out, dout, dq, dk and dv must be 16-byte aligned");
+  if (s.lse && !aligned(s.lse, 4)) return fail(SA_ERR_INVALID_ARG, "lse must be 4-byte aligned");
+  if (s.slopes && !aligned(s.slopes, 4)) return fail(SA_ERR_INVALID_ARG, "alibi_slopes must be 4-byte aligned");
+  const size_t need = bwd_workspace_size(s.B, s.H_q, s.S_q);
+  if (rows) {
+    if (!s.workspace) return fail(SA_ERR_WORKSPACE, "workspace is NULL (%zu bytes needed)", need);
+    if (!aligned(s.workspace, 16)) return fail(SA_ERR_WORKSPACE, "workspace must be 16-byte aligned");
+    if (s.workspace_bytes < need)
+      return fail(SA_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed", s.workspace_bytes, need);
+  }
+  const size_t qb = (size_t)nq * 2, kb = (size_t)nk * 2, lb = (size_t)s.B * s.H_q * s.S_q * 4;
+  const void* ins[8] = {s.q, s.k, s.v, s.out, s.dout, s.lse, s.mask, s.slopes};
+  const size_t insz[8] = {qb, kb, kb, qb, qb, lb, (size_t)s.B * s.S_k, (size_t)s.H_q * 4};
+  const void* outs[4] = {s.dq, s.dk, s.dv, rows ? s.workspace : nullptr};
+  const size_t outsz[4] = {qb, kb, kb, need};
+  for (int o = 0; o < 4; ++o) {
+    for (int i = 0; i < 8; ++i)
+      if (overlap(outs[o], outsz[o], ins[i], insz[i]))
+        return fail(SA_ERR_INVALID_ARG, "dq, dk, dv or workspace overlap an input");
+    for (int o2 = o + 1; o2 < 4; ++o2)
+      if (overlap(outs[o], outsz[o], outs[o2], outsz[o2]))
+        return fail(SA_ERR_INVALID_ARG, "dq, dk, dv and workspace must not overlap");
+  }
+  return SA_OK;
+}
+
 }  // namespace sa

@@ -20,6 +20,14 @@ struct DecodeShape {
   const void* workspace; size_t workspace_bytes;
 };
 
+struct BwdShape {
+  const void* q; const void* k; const void* v; const void* out; const void* dout; const float* lse;
+  const void* dq; const void* dk; const void* dv;
+  int B, S_q, S_k, H_q, H_kv, D; float scale; int causal;
+  const uint8_t* mask; const float* slopes; int dtype;
+  const void* workspace; size_t workspace_bytes;
+};
+
 // Keys one decode split covers at least, and most splits per (batch, KV head,
 // query-head group).  A split is one workgroup of four waves.
 constexpr int kDecodeStepKeys = 128;
@@ -41,6 +49,10 @@ const char* status_string(int status);
 // when the call is valid but has nothing to compute.
 int check_fwd(const FwdShape& s, bool* noop);
 int check_decode(const DecodeShape& s, bool* noop);
+int check_bwd(const BwdShape& s, bool* noop);
+// Bytes of backward workspace: one float2 {lse in base 2, row dot} per
+// (batch, query head, row); 0 for a negative size or on overflow.
+size_t bwd_workspace_size(int B, int H_q, int S_q);
 
 int decode_num_splits(int B, int S_k, int H_q, int H_kv, int num_cu);
 // Waves per prefill workgroup (4 or 8; a workgroup owns 32 query rows per

@@ -134,3 +134,50 @@ def test_decode_splits_and_workspace(L):
         assert sa.decode_workspace_size(B, Hq, S, 64) >= need
     assert sa.decode_workspace_size(-1, 1, 1, 64) == 0
     assert sa.decode_workspace_size(0, 1, 1, 64) >= 0
+
+
+# Backward: more fake buffers beside the forward's.
+DO, DQ, DK, DV = (A + i * (1 << 32) for i in range(7, 11))
+
+
+def bwd(L, q=Q, k=K, v=V, out=O, dout=DO, lse=LSE, dq=DQ, dk=DK, dv=DV, B=1, S_q=8, S_k=8, H_q=2,
+        H_kv=2, D=64, scale=0.125, causal=0, mask=None, slopes=None, dtype=0, ws=WS, wsb=None):
+    if wsb is None:
+        wsb = L.sa_attn_bwd_workspace_size(B, H_q, S_q)
+    return L.sa_attn_bwd(q, k, v, out, dout, lse, dq, dk, dv, B, S_q, S_k, H_q, H_kv, D, scale,
+                         causal, mask, slopes, dtype, ws, wsb, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dout=None), sa.SA_ERR_INVALID_ARG),
+    (dict(dq=None), sa.SA_ERR_INVALID_ARG),
+    (dict(dv=None), sa.SA_ERR_INVALID_ARG),
+    (dict(lse=None), sa.SA_ERR_INVALID_ARG),
+    (dict(dk=DK + 8), sa.SA_ERR_INVALID_ARG),      # misaligned
+    (dict(lse=LSE + 2), sa.SA_ERR_INVALID_ARG),
+    (dict(D=96), sa.SA_ERR_UNSUPPORTED),
+    (dict(dtype=3), sa.SA_ERR_UNSUPPORTED),
+    (dict(H_q=5, H_kv=2), sa.SA_ERR_INVALID_ARG),
+    (dict(S_q=-1), sa.SA_ERR_INVALID_ARG),
+    (dict(causal=-1), sa.SA_ERR_INVALID_ARG),
+    (dict(scale=float("inf")), sa.SA_ERR_INVALID_ARG),
+    (dict(slopes=SL, scale=0.0), sa.SA_ERR_INVALID_ARG),
+    (dict(ws=None), sa.SA_ERR_WORKSPACE),
+    (dict(wsb=8), sa.SA_ERR_WORKSPACE),
+    (dict(ws=WS + 8), sa.SA_ERR_WORKSPACE),
+    (dict(dq=Q), sa.SA_ERR_INVALID_ARG),           # dq aliases q
+    (dict(dk=DO + 64), sa.SA_ERR_INVALID_ARG),     # dk inside dout
+    (dict(dv=DK), sa.SA_ERR_INVALID_ARG),          # dv aliases dk
+    (dict(ws=DQ), sa.SA_ERR_INVALID_ARG),          # workspace aliases dq
+])
+def test_bwd_rejects(L, kw, code):
+    assert bwd(L, **kw) == code
+    assert sa.last_error() != ""
+
+
+def test_bwd_noop_and_workspace(L):
+    assert bwd(L, B=0, q=None, dq=None, ws=None, wsb=0) == sa.SA_OK
+    assert bwd(L, S_q=0, S_k=0, q=None, k=None, dq=None, dk=None, ws=None, wsb=0) == sa.SA_OK
+    # One {lse2, Di} float pair per query row.
+    assert sa.bwd_workspace_size(2, 14, 4096) == 2 * 14 * 4096 * 8
+    assert sa.bwd_workspace_size(-1, 1, 1) == 0

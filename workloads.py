@@ -120,6 +120,14 @@ def make_inputs(w: Workload, seed: Optional[int] = None, scale_qk: float = 1.0) 
     return Inputs(w, q, k, v, mask, slopes, tails)
 
 
+def make_dout(w: Workload, seed: Optional[int] = None) -> torch.Tensor:
+    """Seeded upstream gradient of the output (``[B, S_q, H_q, D]``, N(0, 1)
+    drawn in float32 and cast), for the backward; seed defaults to the
+    workload's seed + 1000."""
+    g = torch.Generator().manual_seed(w.seed + 1000 if seed is None else seed)
+    return torch.randn((w.B, w.S_q, w.H_q, w.D), generator=g).to(DTYPES[w.dtype])
+
+
 def to_f64(t: torch.Tensor) -> np.ndarray:
     """Exact float64 numpy copy of a CPU tensor (fp16/bf16 values are exact in fp64)."""
     return t.detach().to("cpu", torch.float64).numpy()
