@@ -21,6 +21,13 @@ the 2.5 PFLOP/s dense bf16 matrix peak, and ``decode`` carries the decode
 part's key/value read bandwidth against 8 TB/s.  ``cpu_baseline`` times the
 float64 CPU oracle on a bounded sample of the same workloads on this host.
 
+The ``*_bwd`` workloads time the backward instead (``sa_attn_bwd``: the
+per-row pre-pass, the dq kernel and the dk/dv kernel) on the same inputs,
+with ``out`` and ``lse`` from one forward call made before timing.  Their
+FLOPs are the five products per visible query-key pair (S recomputed, dP, dV,
+dK, dQ: 10 * D per pair, 2.5 times the forward's count), and their
+``roofline`` is the whole call against the matrix peak.
+
 Prints one JSON line on stdout.  Only one GPU is supported: --gpus above 1
 exits with a message.
 """
@@ -47,6 +54,7 @@ PROFILES = ROOT / "profiles"
 KERNEL_SOURCES = {
     "fwd_kernel": ["common.hpp", "prefill.hpp", "sa_attn.hip"],
     "decode_kernel": ["common.hpp", "host_logic.hpp", "decode.hpp", "sa_attn.hip"],
+    "bwd_kernels": ["common.hpp", "host_logic.hpp", "backward.hpp", "sa_attn_bwd.hip"],
 }
 
 STEPS = {
@@ -57,6 +65,8 @@ STEPS = {
     "c4_decode_32k": ["c4_decode_32k"],
     "c2_causal_pad16": ["c2_causal_pad16"],
     "c1_fwd_256": ["c1_fwd_256"],
+    "c3_causal_4096_bwd": ["c3_causal_4096:bwd"],
+    "c5_alibi_8192_bwd": ["c5_alibi_8192:bwd"],
 }
 
 
@@ -74,8 +84,9 @@ def visible_pairs(w, tails):
     return total
 
 
-def algorithmic_flops(w, tails):
-    return 4 * w.D * w.H_q * visible_pairs(w, tails)
+def algorithmic_flops(w, tails, bwd=False):
+    """4 * D FLOPs per visible pair forward (two products), 10 * D backward (five)."""
+    return (10 if bwd else 4) * w.D * w.H_q * visible_pairs(w, tails)
 
 
 def kv_bytes(w):
@@ -111,7 +122,9 @@ class Part:
     def __init__(self, name, dev):
         import torch
         import online_softmax_amd as sa
-        from workloads import WORKLOADS, make_inputs
+        from workloads import WORKLOADS, make_dout, make_inputs
+        name, _, mode = name.partition(":")
+        self.bwd = mode == "bwd"
         self.w = w = WORKLOADS[name]
         self.sa = sa
         inp = make_inputs(w)
@@ -127,14 +140,28 @@ class Part:
             self.ks, self.vs = [d(inp.k)], [d(inp.v)]
             self.lse = torch.empty((w.B, w.H_q, w.S_q), dtype=torch.float32, device=dev)
         self.out = torch.empty_like(self.q)
-        self.flops = algorithmic_flops(w, self.tails)
+        self.flops = algorithmic_flops(w, self.tails, self.bwd)
         self.calls = 0
+        if self.bwd:
+            sa.attn_fwd(self.q, self.ks[0], self.vs[0], causal=w.causal, scale=w.scale,
+                        key_padding_mask=self.mask, alibi_slopes=self.slopes, out=self.out,
+                        lse=self.lse)
+            self.dout = d(make_dout(w))
+            self.dq = torch.empty_like(self.q)
+            self.dk, self.dv = torch.empty_like(self.ks[0]), torch.empty_like(self.vs[0])
+            self.ws = torch.empty(sa.bwd_workspace_size(w.B, w.H_q, w.S_q), dtype=torch.uint8,
+                                  device=dev)
         del inp
 
     def run(self):
         w, i = self.w, self.calls % len(self.ks)
         self.calls += 1
-        if w.decode:
+        if self.bwd:
+            self.sa.attn_bwd(self.q, self.ks[0], self.vs[0], self.out, self.dout, self.lse,
+                             causal=w.causal, scale=w.scale, key_padding_mask=self.mask,
+                             alibi_slopes=self.slopes, dq=self.dq, dk=self.dk, dv=self.dv,
+                             workspace=self.ws)
+        elif w.decode:
             self.sa.attn_decode(self.q, self.ks[i], self.vs[i], scale=w.scale,
                                 key_padding_mask=self.mask, alibi_slopes=self.slopes,
                                 out=self.out, lse=self.lse, workspace=self.ws)
@@ -165,6 +192,11 @@ def cpu_baseline(parts, budget_s):
         mask = None if inp.mask is None else inp.mask.numpy()
         sl = None if inp.slopes is None else inp.slopes.numpy()
         causal = w.causal and not w.decode
+        if p.bwd:
+            f, t, desc = _cpu_bwd_sample(p, inp, q, k, v, mask, sl, per_part)
+            flops, secs = flops + f, secs + t
+            samples.append(desc)
+            continue
         # Grow an evenly spaced row sample until the part has used its budget.
         n_rows, used, done_rows = 1, 0.0, 0
         while used < per_part and done_rows < w.S_q:
@@ -185,6 +217,34 @@ def cpu_baseline(parts, budget_s):
         samples.append(f"{w.name}: {done_rows} of {w.S_q} query rows x all batches and heads")
     return {"value": flops / secs / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
             "sample": "; ".join(samples) + f" ({secs:.1f} s of float64 numpy)"}
+
+
+def _cpu_bwd_sample(p, inp, q, k, v, mask, sl, budget_s):
+    """Oracle backward over whole (batch row, query head) pairs until the budget is used."""
+    import oracle
+    from workloads import make_dout, to_f64
+    w = p.w
+    do = to_f64(make_dout(w))
+    flops, used, n = 0, 0.0, 0
+    G = w.H_q // w.H_kv
+    while used < budget_s and n < w.B * w.H_q:
+        b, h = n % w.B, (n // w.B) % w.H_q
+        hk = h // G
+        t0 = time.perf_counter()
+        oracle.attention_bwd(q[b:b + 1, :, h:h + 1], k[b:b + 1, :, hk:hk + 1], v[b:b + 1, :, hk:hk + 1],
+                             do[b:b + 1, :, h:h + 1], w.scale, causal=w.causal,
+                             key_padding_mask=None if mask is None else mask[b:b + 1],
+                             alibi_slopes=None if sl is None else sl[h:h + 1])
+        used += time.perf_counter() - t0
+        flops += 10 * w.D * visible_pairs(OneRow(w), [inp.tails[b]] if inp.tails else [])
+        n += 1
+    return flops, used, f"{w.name} backward: {n} of {w.B * w.H_q} (batch row, head) pairs, whole rows"
+
+
+class OneRow:
+    """One batch row of a workload (for counting its visible pairs)."""
+    def __init__(self, w):
+        self.B, self.S_q, self.S_k, self.causal = 1, w.S_q, w.S_k, w.causal
 
 
 def copy_calibration(args, dev):
@@ -286,15 +346,25 @@ def main():
         "dtype": parts[0].w.dtype if parts[0].w.dtype != "fp16" else "fp16",
         "data": "synthetic (seeded N(0,1) q/k/v)",
         "config": {"workload": args.workload,
-                   "parts": [f"{p.w.name}: B={p.w.B} S_q={p.w.S_q} S_k={p.w.S_k} H_q={p.w.H_q} "
+                   "parts": [f"{p.w.name}{' backward' if p.bwd else ''}: B={p.w.B} S_q={p.w.S_q} S_k={p.w.S_k} H_q={p.w.H_q} "
                              f"H_kv={p.w.H_kv} D={p.w.D} {p.w.dtype} causal={p.w.causal} "
                              f"mask={'tails ' + str(p.tails) if p.tails else 'none'} "
                              f"alibi={p.w.alibi}" for p in parts],
                    "wall_s_lead_plus_timed": round(wall, 4),
                    "device_lead_ms": round(n_lead * mm_ms, 3)},
     }
-    prefill = [(p, t) for p, t in zip(parts, part_ms) if not p.w.decode]
+    prefill = [(p, t) for p, t in zip(parts, part_ms) if not p.w.decode and not p.bwd]
     decode = [(p, t) for p, t in zip(parts, part_ms) if p.w.decode]
+    backward = [(p, t) for p, t in zip(parts, part_ms) if p.bwd]
+    if backward:
+        p, t = backward[0]
+        ach = p.flops / (t * 1e-3) / 1e12
+        result["roofline"] = {"bound": "mfma", "achieved": round(ach, 2), "peak": MFMA_PEAK_TFLOPS,
+                              "unit": "TFLOP/s", "frac": round(ach / MFMA_PEAK_TFLOPS, 4),
+                              "traffic": read_traffic("bwd_kernels", p.w.name),
+                              "kernel": "bwd_pre_kernel + bwd_dq_kernel + bwd_dkdv_kernel (one call)",
+                              "workload": p.w.name + " backward", "avg_call_ms": round(t, 4),
+                              "flops_per_call": p.flops}
     if prefill:
         p, t = max(prefill, key=lambda x: x[1])
         ach = p.flops / (t * 1e-3) / 1e12

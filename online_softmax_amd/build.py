@@ -12,6 +12,7 @@ import os
 import shutil
 import subprocess
 import sys
+from concurrent.futures import ThreadPoolExecutor
 from pathlib import Path
 
 PKG = Path(__file__).resolve().parent
@@ -25,6 +26,9 @@ ARCH = "gfx950"
 HIP_FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
              "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
              "-Wall", "-Wno-unused-function"]
+# The backward's unit keeps MFMA results in ordinary vector registers (see
+# the header of sa_attn_bwd.hip).
+BWD_FLAGS = ["-mllvm", "-amdgpu-mfma-vgpr-form"]
 
 
 def _hipcc() -> str:
@@ -53,13 +57,18 @@ def build(verbose: bool = False) -> Path:
     BUILD.mkdir(exist_ok=True)
     host_o = BUILD / "host_logic.o"
     dev_o = BUILD / "sa_attn.o"
-    for p in (host_o, dev_o):
+    bwd_o = BUILD / "sa_attn_bwd.o"
+    for p in (host_o, dev_o, bwd_o):
         if p.exists():
             p.unlink()
-    _run(["g++", "-O2", "-std=c++17", "-fPIC", "-Wall", "-c", CSRC / "host_logic.cpp", "-o", host_o], verbose)
-    _run([hipcc, *HIP_FLAGS, "-c", CSRC / "sa_attn.hip", "-o", dev_o], verbose)
+    steps = [["g++", "-O2", "-std=c++17", "-fPIC", "-Wall", "-c", CSRC / "host_logic.cpp", "-o", host_o],
+             [hipcc, *HIP_FLAGS, "-c", CSRC / "sa_attn.hip", "-o", dev_o],
+             [hipcc, *HIP_FLAGS, *BWD_FLAGS, "-c", CSRC / "sa_attn_bwd.hip", "-o", bwd_o]]
+    with ThreadPoolExecutor(len(steps)) as pool:
+        for f in [pool.submit(_run, cmd, verbose) for cmd in steps]:
+            f.result()
     tmp = LIB.with_suffix(".so.tmp")
-    _run([hipcc, "-shared", f"--offload-arch={ARCH}", "-o", tmp, dev_o, host_o], verbose)
+    _run([hipcc, "-shared", f"--offload-arch={ARCH}", "-o", tmp, dev_o, bwd_o, host_o], verbose)
     os.replace(tmp, LIB)
     return LIB
 

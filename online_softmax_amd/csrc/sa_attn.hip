@@ -1,7 +1,7 @@
 // libsa_attn: C ABI entry points, kernel selection and launches.
 //
 // Everything here is host code around the kernels of prefill.hpp and
-// decode.hpp: validate (host_logic.cpp, no HIP call), pick the template
+// decode.hpp (the backward's entry points are in sa_attn_bwd.hip): validate (host_logic.cpp, no HIP call), pick the template
 // instance for {dtype, D, causal, mask, ALiBi}, launch on the caller's stream.
 #include <hip/hip_runtime.h>
 
@@ -9,9 +9,9 @@
 #include <mutex>
 
 #include "../../include/sa_attn.h"
-#include "backward.hpp"
 #include "decode.hpp"
 #include "host_logic.hpp"
+#include "launch.hpp"
 #include "prefill.hpp"
 
 namespace sa {
@@ -37,11 +37,6 @@ int num_cus(int* out) {
   return SA_OK;
 }
 
-int launched(const char* what) {
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return fail(SA_ERR_HIP, "%s launch failed: %s", what, hipGetErrorString(e));
-  return SA_OK;
-}
 
 template <class T, int D, bool C, bool M, bool A>
 void launch_fwd(const FwdArgs& args, int nw, hipStream_t st) {
@@ -77,30 +72,6 @@ void dispatch_decode(const DecArgs& args, const MergeArgs& margs, int nwg, bool 
     default: hipLaunchKernelGGL((decode_kernel<T, D, true, true>), dim3(nwg), dim3(256), 0, st, args); break;
   }
   hipLaunchKernelGGL((decode_merge_kernel<T, D>), dim3(args.B * args.H_q * (D / 16)), dim3(256), 0, st, margs);
-}
-
-template <class T, int D, bool C, bool M, bool A>
-void launch_bwd_main(const BwdArgs& args, hipStream_t st) {
-  const int ndq = args.B * args.H_q * args.nqb, ndk = args.B * args.H_kv * args.nkb;
-  if (ndq > 0) hipLaunchKernelGGL((bwd_dq_kernel<T, D, C, M, A>), dim3(ndq), dim3(256), 0, st, args);
-  if (ndk > 0) hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, C, M, A>), dim3(ndk), dim3(256), 0, st, args);
-}
-
-template <class T, int D>
-void dispatch_bwd(const BwdArgs& args, bool causal, bool mask, bool alibi, hipStream_t st) {
-  const int64_t rows = (int64_t)args.B * args.H_q * args.S_q;
-  if (rows > 0) hipLaunchKernelGGL((bwd_pre_kernel<T, D>), dim3((unsigned)((rows + 255) / 256)), dim3(256), 0, st, args);
-  const int key = (causal ? 4 : 0) | (mask ? 2 : 0) | (alibi ? 1 : 0);
-  switch (key) {
-    case 0: launch_bwd_main<T, D, false, false, false>(args, st); break;
-    case 1: launch_bwd_main<T, D, false, false, true>(args, st); break;
-    case 2: launch_bwd_main<T, D, false, true, false>(args, st); break;
-    case 3: launch_bwd_main<T, D, false, true, true>(args, st); break;
-    case 4: launch_bwd_main<T, D, true, false, false>(args, st); break;
-    case 5: launch_bwd_main<T, D, true, false, true>(args, st); break;
-    case 6: launch_bwd_main<T, D, true, true, false>(args, st); break;
-    default: launch_bwd_main<T, D, true, true, true>(args, st); break;
-  }
 }
 
 }  // namespace
@@ -217,53 +188,6 @@ int sa_attn_decode(const void* q, const void* k_cache, const void* v_cache, void
     else dispatch_decode<BF16, 128>(args, margs, (int)nwg, m, al, hs);
   }
   return launched("decode");
-}
-
-size_t sa_attn_bwd_workspace_size(int B, int H_q, int S_q) { return sa::bwd_workspace_size(B, H_q, S_q); }
-
-int sa_attn_bwd(const void* q, const void* k, const void* v, const void* out, const void* dout,
-                const float* lse, void* dq, void* dk, void* dv, int B, int S_q, int S_k, int H_q,
-                int H_kv, int D, float scale, int causal, const uint8_t* key_padding_mask,
-                const float* alibi_slopes, int dtype, void* workspace, size_t workspace_bytes,
-                sa_stream_t stream) {
-  using namespace sa;
-  clear_error();
-  BwdShape shp{q, k, v, out, dout, lse, dq, dk, dv, B, S_q, S_k, H_q, H_kv, D, scale, causal,
-               key_padding_mask, alibi_slopes, dtype, workspace, workspace_bytes};
-  bool noop = false;
-  int st = check_bwd(shp, &noop);
-  if (st != SA_OK || noop) return st;
-
-  BwdArgs args;
-  args.q = (const uint16_t*)q;
-  args.k = (const uint16_t*)k;
-  args.v = (const uint16_t*)v;
-  args.out = (const uint16_t*)out;
-  args.dout = (const uint16_t*)dout;
-  args.lse = lse;
-  args.dq = (uint16_t*)dq;
-  args.dk = (uint16_t*)dk;
-  args.dv = (uint16_t*)dv;
-  args.mask = key_padding_mask;
-  args.slopes = alibi_slopes;
-  args.ld = (float2*)workspace;
-  args.B = B; args.S_q = S_q; args.S_k = S_k; args.H_q = H_q; args.H_kv = H_kv;
-  args.G = H_q / H_kv;
-  args.scale = scale;
-  args.scale2 = std::fabs(scale) * kLog2e;
-  args.alibi2 = scale != 0.f ? 1.0f / std::fabs(scale) : 0.f;
-  args.nqb = (S_q + 127) / 128;
-  args.nkb = (S_k + 127) / 128;
-  const bool c = causal != 0, m = key_padding_mask != nullptr, al = alibi_slopes != nullptr;
-  hipStream_t hs = (hipStream_t)stream;
-  if (dtype == SA_F16) {
-    if (D == 64) dispatch_bwd<F16, 64>(args, c, m, al, hs);
-    else dispatch_bwd<F16, 128>(args, c, m, al, hs);
-  } else {
-    if (D == 64) dispatch_bwd<BF16, 64>(args, c, m, al, hs);
-    else dispatch_bwd<BF16, 128>(args, c, m, al, hs);
-  }
-  return launched("attention backward");
 }
 
 const char* sa_status_string(int status) { return sa::status_string(status); }
