@@ -17,6 +17,10 @@ fast:
 * ``attention_bwd`` — the gradients dq, dk, dv of the attention output by
   their definition (the single-sweep backward of the "StreamAttention" page,
   "Recent Updates"; "flash-attn-volta" page, "Backward correctness").
+* ``block_sparse_attention`` — attention restricted to selected (query block,
+  key block) pairs, the execution step of the "Stem" page (section 2.3),
+  written as its pseudo-sparse fallback: the block selection expanded into an
+  element mask, then the definition above.
 * ``merge_states`` — the log-sum-exp weighted combination of partial states
   ("StreamAttention" page, "Engine Direction" and "Distributed and
   Long-Context Variants").
@@ -26,9 +30,11 @@ Every function here is pinned by tests that do not go through the oracle's own
 code path (closed forms, invariants, a library routine, brute force); none of
 them is "parity unpinned".
 """
-from .attention import (attention, attention_bwd, attention_probs, online_attention,
-                        merge_states, partial_state, alibi_bias, visible)
+from .attention import (SPARSE_BLOCK, attention, attention_bwd, attention_probs,
+                        block_sparse_attention, online_attention, merge_states, partial_state,
+                        alibi_bias, visible)
 from . import brute
 
-__all__ = ["attention", "attention_bwd", "attention_probs", "online_attention", "merge_states",
+__all__ = ["SPARSE_BLOCK", "attention", "attention_bwd", "attention_probs", "block_sparse_attention",
+           "online_attention", "merge_states",
            "partial_state", "alibi_bias", "visible", "brute"]

@@ -127,6 +127,65 @@ def attention(q, k, v, scale, causal=False, key_padding_mask=None,
     return out, lse
 
 
+# Block size of the block-sparse selection: the default attention block of
+# the "Stem: Rethinking Causal Information Flow in Sparse Attention" page
+# (section 6, parameter table, ``block_size``), for query rows and keys alike.
+SPARSE_BLOCK = 128
+
+
+def expand_block_mask(block_mask_bh, S_q, S_k, rows=None, block=SPARSE_BLOCK):
+    """``[R, S_k]`` boolean: row i may see key j when the block pair
+    ``(i // block, j // block)`` is selected in ``block_mask_bh``
+    (``[ceil(S_q / block), ceil(S_k / block)]``, nonzero = selected)."""
+    rows = np.arange(S_q) if rows is None else np.asarray(rows)
+    bm = np.asarray(block_mask_bh) != 0
+    return bm[rows // block][:, np.arange(S_k) // block]
+
+
+def block_sparse_attention(q, k, v, scale, block_mask, causal=False,
+                           key_padding_mask=None, alibi_slopes=None, rows=None,
+                           block=SPARSE_BLOCK):
+    """Attention restricted to selected (query block, key block) pairs.
+
+    The execution step of the "Stem" page (section 2.3, "Block-Sparse
+    Attention"): each block of query rows attends only to the key blocks
+    chosen for it.  Its fallback, the "pseudo-sparse" run, expands the block
+    selection into an element mask and runs dense attention; that is what this
+    function does, so a row sees key j when j passes the causal rule and the
+    padding mask of ``attention`` *and* j's block is selected for the row's
+    block.  ``block_mask``: ``[B, H_q, ceil(S_q / block), ceil(S_k / block)]``,
+    nonzero = selected.  A row left with no visible key gets out = 0 and
+    lse = -inf.  Returns ``out [B, R, H_q, D]`` and ``lse [B, H_q, R]``.
+    """
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    B, S_q, H_q, D = q.shape
+    S_k, H_kv = k.shape[1], k.shape[2]
+    if H_q % H_kv:
+        raise ValueError("H_q must be a multiple of H_kv")
+    bm = np.asarray(block_mask)
+    nbq, nbk = -(-S_q // block), -(-S_k // block)
+    if bm.shape != (B, H_q, nbq, nbk):
+        raise ValueError(f"block_mask shape {bm.shape} != {(B, H_q, nbq, nbk)}")
+    G = H_q // H_kv
+    rows = np.arange(S_q) if rows is None else np.asarray(rows, dtype=np.int64)
+    R = len(rows)
+    out = np.zeros((B, R, H_q, D))
+    lse = np.full((B, H_q, R), -np.inf)
+    for b in range(B):
+        mrow = None if key_padding_mask is None else np.asarray(key_padding_mask)[b]
+        keep = visible(S_q, S_k, causal, mrow, rows)
+        for h in range(H_q):
+            hk = h // G
+            keep_h = keep & expand_block_mask(bm[b, h], S_q, S_k, rows, block)
+            bias = None
+            if alibi_slopes is not None:
+                bias = alibi_bias(np.asarray(alibi_slopes, np.float64)[h], S_q, S_k, rows)
+            s = _scores(q[b, rows, h, :], k[b, :, hk, :], scale, keep_h, bias)
+            P, lse[b, h] = _softmax_rows(s)
+            out[b, :, h, :] = P @ v[b, :, hk, :]
+    return out, lse
+
+
 def attention_probs(q, k, scale, b, h, causal=False, key_padding_mask=None,
                     alibi_slopes=None):
     """The full probability matrix ``P [S_q, S_k]`` of one (b, h)."""

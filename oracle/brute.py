@@ -13,8 +13,12 @@ import math
 
 
 def attention(q, k, v, scale, causal=False, key_padding_mask=None,
-              alibi_slopes=None):
+              alibi_slopes=None, block_mask=None, block=128):
     """q: nested ``[B][S_q][H_q][D]``; k, v: ``[B][S_k][H_kv][D]``.
+
+    ``block_mask`` (nested ``[B][H_q][query block][key block]``, truthy =
+    selected) restricts row i to keys whose block of ``block`` keys is
+    selected for the block of ``block`` rows holding i.
 
     Returns ``(out [B][S_q][H_q][D], lse [B][H_q][S_q])`` as Python floats.
     """
@@ -33,6 +37,8 @@ def attention(q, k, v, scale, causal=False, key_padding_mask=None,
                     if causal and j > pos:
                         continue
                     if key_padding_mask is not None and not key_padding_mask[b][j]:
+                        continue
+                    if block_mask is not None and not block_mask[b][h][i // block][j // block]:
                         continue
                     dot = math.fsum(float(q[b][i][h][d]) * float(k[b][j][hk][d])
                                     for d in range(D))
