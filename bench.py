@@ -21,6 +21,12 @@ the 2.5 PFLOP/s dense bf16 matrix peak, and ``decode`` carries the decode
 part's key/value read bandwidth against 8 TB/s.  ``cpu_baseline`` times the
 float64 CPU oracle on a bounded sample of the same workloads on this host.
 
+The ``*_sparse`` workload times the block-sparse forward
+(``sa_attn_fwd_block_sparse``) on the same inputs with a seeded selection of
+128 x 128 blocks shaped like the Stem page's (4 sink blocks, a 4-block
+window, 20 % of the rest); its FLOPs count only the visible pairs of the
+selected blocks.
+
 The ``*_bwd`` workloads time the backward instead (``sa_attn_bwd``: the
 per-row pre-pass, the dq kernel and the dk/dv kernel) on the same inputs,
 with ``out`` and ``lse`` from one forward call made before timing.  Their
@@ -65,6 +71,7 @@ STEPS = {
     "c4_decode_32k": ["c4_decode_32k"],
     "c2_causal_pad16": ["c2_causal_pad16"],
     "c1_fwd_256": ["c1_fwd_256"],
+    "c5_alibi_8192_sparse": ["c5_alibi_8192:sparse"],
     "c3_causal_4096_bwd": ["c3_causal_4096:bwd"],
     "c5_alibi_8192_bwd": ["c5_alibi_8192:bwd"],
 }
@@ -87,6 +94,32 @@ def visible_pairs(w, tails):
 def algorithmic_flops(w, tails, bwd=False):
     """4 * D FLOPs per visible pair forward (two products), 10 * D backward (five)."""
     return (10 if bwd else 4) * w.D * w.H_q * visible_pairs(w, tails)
+
+
+def sparse_row_block_keys(w, tails, rows=None, block=128):
+    """[B, R, nbk]: keys of key block y that row i may see under the causal
+    rule and the padding tail (before the block selection)."""
+    import numpy as np
+    rows = np.arange(w.S_q) if rows is None else np.asarray(rows)
+    nbk = -(-w.S_k // block)
+    y0 = np.arange(nbk) * block
+    out = np.zeros((w.B, len(rows), nbk), dtype=np.int64)
+    for b in range(w.B):
+        t = tails[b] if tails else 0
+        last = np.full(len(rows), w.S_k - t - 1)
+        if w.causal:
+            last = np.minimum(last, rows + (w.S_k - w.S_q))
+        out[b] = np.clip(last[:, None] + 1 - y0[None, :], 0, block)
+    return out
+
+
+def sparse_flops(w, tails, bm, rows=None, block=128):
+    """4 * D per visible pair of the selected blocks (bm: [B, H_q, nbq, nbk])."""
+    import numpy as np
+    rows = np.arange(w.S_q) if rows is None else np.asarray(rows)
+    cnt = sparse_row_block_keys(w, tails, rows, block)          # [B, R, nbk]
+    sel = np.asarray(bm)[:, :, rows // block, :].astype(np.int64)  # [B, H, R, nbk]
+    return 4 * w.D * int((sel * cnt[:, None]).sum())
 
 
 def kv_bytes(w):
@@ -122,9 +155,10 @@ class Part:
     def __init__(self, name, dev):
         import torch
         import online_softmax_amd as sa
-        from workloads import WORKLOADS, make_dout, make_inputs
+        from workloads import WORKLOADS, make_block_mask, make_dout, make_inputs
         name, _, mode = name.partition(":")
         self.bwd = mode == "bwd"
+        self.sparse = mode == "sparse"
         self.w = w = WORKLOADS[name]
         self.sa = sa
         inp = make_inputs(w)
@@ -142,6 +176,10 @@ class Part:
         self.out = torch.empty_like(self.q)
         self.flops = algorithmic_flops(w, self.tails, self.bwd)
         self.calls = 0
+        if self.sparse:
+            self.bm_cpu = make_block_mask(w)
+            self.bm = d(self.bm_cpu)
+            self.flops = sparse_flops(w, self.tails, self.bm_cpu.numpy())
         if self.bwd:
             sa.attn_fwd(self.q, self.ks[0], self.vs[0], causal=w.causal, scale=w.scale,
                         key_padding_mask=self.mask, alibi_slopes=self.slopes, out=self.out,
@@ -161,6 +199,10 @@ class Part:
                              causal=w.causal, scale=w.scale, key_padding_mask=self.mask,
                              alibi_slopes=self.slopes, dq=self.dq, dk=self.dk, dv=self.dv,
                              workspace=self.ws)
+        elif self.sparse:
+            self.sa.attn_fwd_block_sparse(self.q, self.ks[0], self.vs[0], self.bm, causal=w.causal,
+                                          scale=w.scale, key_padding_mask=self.mask,
+                                          alibi_slopes=self.slopes, out=self.out, lse=self.lse)
         elif w.decode:
             self.sa.attn_decode(self.q, self.ks[i], self.vs[i], scale=w.scale,
                                 key_padding_mask=self.mask, alibi_slopes=self.slopes,
@@ -203,6 +245,14 @@ def cpu_baseline(parts, budget_s):
             n = min(n_rows, w.S_q - done_rows)
             rows = (np.arange(done_rows, done_rows + n) * 7919) % w.S_q
             t0 = time.perf_counter()
+            if p.sparse:
+                oracle.block_sparse_attention(q, k, v, w.scale, p.bm_cpu.numpy(), causal=causal,
+                                              key_padding_mask=mask, alibi_slopes=sl, rows=rows)
+                used += time.perf_counter() - t0
+                flops += sparse_flops(w, inp.tails, p.bm_cpu.numpy(), rows)
+                done_rows += n
+                n_rows *= 2
+                continue
             oracle.attention(q, k, v, w.scale, causal=causal, key_padding_mask=mask,
                              alibi_slopes=sl, rows=rows)
             used += time.perf_counter() - t0
@@ -346,7 +396,8 @@ def main():
         "dtype": parts[0].w.dtype if parts[0].w.dtype != "fp16" else "fp16",
         "data": "synthetic (seeded N(0,1) q/k/v)",
         "config": {"workload": args.workload,
-                   "parts": [f"{p.w.name}{' backward' if p.bwd else ''}: B={p.w.B} S_q={p.w.S_q} S_k={p.w.S_k} H_q={p.w.H_q} "
+                   "parts": [f"{p.w.name}{' backward' if p.bwd else ''}"
+                             f"{' block-sparse (%.1f %% of blocks selected)' % (100 * p.bm_cpu.float().mean().item()) if p.sparse else ''}: B={p.w.B} S_q={p.w.S_q} S_k={p.w.S_k} H_q={p.w.H_q} "
                              f"H_kv={p.w.H_kv} D={p.w.D} {p.w.dtype} causal={p.w.causal} "
                              f"mask={'tails ' + str(p.tails) if p.tails else 'none'} "
                              f"alibi={p.w.alibi}" for p in parts],
@@ -371,7 +422,8 @@ def main():
         result["roofline"] = {"bound": "mfma", "achieved": round(ach, 2), "peak": MFMA_PEAK_TFLOPS,
                               "unit": "TFLOP/s", "frac": round(ach / MFMA_PEAK_TFLOPS, 4),
                               "traffic": read_traffic("fwd_kernel", p.w.name),
-                              "kernel": "fwd_kernel", "workload": p.w.name,
+                              "kernel": "fwd_kernel" + (" (block-sparse)" if p.sparse else ""),
+                              "workload": p.w.name + (" block-sparse" if p.sparse else ""),
                               "avg_launch_ms": round(t, 4), "flops_per_launch": p.flops,
                               "dense_count_tflops": round(4 * p.w.B * p.w.H_q * p.w.S_q * p.w.S_k * p.w.D
                                                           / (t * 1e-3) / 1e12, 2)}

@@ -86,6 +86,31 @@ int sa_attn_fwd(const void* q, const void* k, const void* v, void* out, float* l
                 int dtype, sa_stream_t stream);
 
 /*
+ * Block-sparse attention forward: sa_attn_fwd in which each block of 128
+ * query rows attends only to the blocks of 128 keys selected for it (the
+ * execution step of the "Stem: Rethinking Causal Information Flow in Sparse
+ * Attention" page, section 2.3, with its default block_size of 128 from
+ * section 6).  Key j is visible to row i when sa_attn_fwd's rules keep it
+ * (causal, padding) and block_mask[b][h][i / 128][j / 128] is nonzero; the
+ * result equals dense attention with that element mask (the page's
+ * "pseudo-sparse" run), and only the selected key/value tiles are read.
+ *
+ *   block_mask [B, H_q, ceil(S_q / 128), ceil(S_k / 128)] uint8, device,
+ *              nonzero = visit; may be NULL only when S_k == 0
+ *   all other arguments, layouts and rules as in sa_attn_fwd
+ *
+ * A row left with no visible key gets out = 0 and lse = -inf.  Supports
+ * S_k <= 262144 (SA_ERR_UNSUPPORTED beyond).  B == 0 or S_q == 0 is a
+ * successful no-op.  Errors: SA_ERR_INVALID_ARG (also when out or lse
+ * overlaps the block mask), SA_ERR_UNSUPPORTED, SA_ERR_HIP.
+ */
+int sa_attn_fwd_block_sparse(const void* q, const void* k, const void* v, void* out, float* lse,
+                             int B, int S_q, int S_k, int H_q, int H_kv, int D, float scale,
+                             int causal, const uint8_t* key_padding_mask,
+                             const float* alibi_slopes, const uint8_t* block_mask, int dtype,
+                             sa_stream_t stream);
+
+/*
  * Bytes of device workspace sa_attn_decode needs for these sizes (an upper
  * bound that holds for every H_kv dividing H_q).  Pure host arithmetic: no
  * HIP call.  Returns 0 when a size is negative or the result would overflow.

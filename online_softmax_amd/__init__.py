@@ -37,6 +37,8 @@ _VP, _FP, _U8P = ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p
 _I, _F, _SZ = ctypes.c_int, ctypes.c_float, ctypes.c_size_t
 SIGNATURES = {
     "sa_attn_fwd": (_I, [_VP, _VP, _VP, _VP, _FP, _I, _I, _I, _I, _I, _I, _F, _I, _U8P, _FP, _I, _VP]),
+    "sa_attn_fwd_block_sparse": (_I, [_VP, _VP, _VP, _VP, _FP, _I, _I, _I, _I, _I, _I, _F, _I, _U8P, _FP,
+                                      _U8P, _I, _VP]),
     "sa_attn_decode_workspace_size": (_SZ, [_I, _I, _I, _I]),
     "sa_attn_decode": (_I, [_VP, _VP, _VP, _VP, _FP, _I, _I, _I, _I, _I, _F, _U8P, _FP, _I, _VP, _SZ, _VP]),
     "sa_attn_decode_num_splits": (_I, [_I, _I, _I, _I, _I]),
@@ -119,17 +121,8 @@ def _mask_arg(mask, B, S_k, dev):
     return mask
 
 
-def attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = False,
-             scale: Optional[float] = None, key_padding_mask: Optional[torch.Tensor] = None,
-             alibi_slopes: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
-             lse: Optional[torch.Tensor] = None, return_lse: bool = True):
-    """Attention forward through ``sa_attn_fwd``.
-
-    q ``[B, S_q, H_q, D]``, k/v ``[B, S_k, H_kv, D]`` (fp16 or bf16, same
-    device); key_padding_mask ``[B, S_k]`` bool/uint8 (nonzero keeps);
-    alibi_slopes float32 ``[H_q]``.  Returns ``out`` (and float32 ``lse``
-    ``[B, H_q, S_q]`` when ``return_lse``).
-    """
+def _fwd_prepare(q, k, v, key_padding_mask, alibi_slopes, out, lse, return_lse, scale):
+    """Checks and output allocation shared by the two forwards."""
     _need(q, "q")
     if q.dtype not in _DTYPE:
         raise ValueError(f"unsupported dtype {q.dtype}")
@@ -151,9 +144,55 @@ def attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = F
     if lse is not None:
         _need(lse, "lse", torch.float32, (B, H_q, S_q), dev)
     sc = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    return dev, (B, S_q, S_k, H_q, H_kv, D), mask, out, lse, sc
+
+
+def attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = False,
+             scale: Optional[float] = None, key_padding_mask: Optional[torch.Tensor] = None,
+             alibi_slopes: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
+             lse: Optional[torch.Tensor] = None, return_lse: bool = True):
+    """Attention forward through ``sa_attn_fwd``.
+
+    q ``[B, S_q, H_q, D]``, k/v ``[B, S_k, H_kv, D]`` (fp16 or bf16, same
+    device); key_padding_mask ``[B, S_k]`` bool/uint8 (nonzero keeps);
+    alibi_slopes float32 ``[H_q]``.  Returns ``out`` (and float32 ``lse``
+    ``[B, H_q, S_q]`` when ``return_lse``).
+    """
+    dev, (B, S_q, S_k, H_q, H_kv, D), mask, out, lse, sc = _fwd_prepare(
+        q, k, v, key_padding_mask, alibi_slopes, out, lse, return_lse, scale)
     st = lib().sa_attn_fwd(q.data_ptr(), _ptr(k), _ptr(v), out.data_ptr(), _ptr(lse),
                            B, S_q, S_k, H_q, H_kv, D, sc, int(bool(causal)), _ptr(mask),
                            _ptr(alibi_slopes), _DTYPE[q.dtype], _stream(dev))
+    _check(st)
+    return (out, lse) if return_lse else out
+
+
+SPARSE_BLOCK = 128  # query rows and keys per block of the block-sparse forward
+
+
+def attn_fwd_block_sparse(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                          block_mask: torch.Tensor, causal: bool = False,
+                          scale: Optional[float] = None,
+                          key_padding_mask: Optional[torch.Tensor] = None,
+                          alibi_slopes: Optional[torch.Tensor] = None,
+                          out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+                          return_lse: bool = True):
+    """Block-sparse attention forward through ``sa_attn_fwd_block_sparse``.
+
+    As ``attn_fwd``, with ``block_mask`` bool/uint8
+    ``[B, H_q, ceil(S_q / 128), ceil(S_k / 128)]`` (nonzero = the query block
+    attends to the key block).
+    """
+    dev, (B, S_q, S_k, H_q, H_kv, D), mask, out, lse, sc = _fwd_prepare(
+        q, k, v, key_padding_mask, alibi_slopes, out, lse, return_lse, scale)
+    if block_mask.dtype == torch.bool:
+        block_mask = block_mask.view(torch.uint8)
+    nbq, nbk = -(-S_q // SPARSE_BLOCK), -(-S_k // SPARSE_BLOCK)
+    _need(block_mask, "block_mask", torch.uint8, (B, H_q, nbq, nbk), dev)
+    st = lib().sa_attn_fwd_block_sparse(q.data_ptr(), _ptr(k), _ptr(v), out.data_ptr(), _ptr(lse),
+                                        B, S_q, S_k, H_q, H_kv, D, sc, int(bool(causal)),
+                                        _ptr(mask), _ptr(alibi_slopes), block_mask.data_ptr(),
+                                        _DTYPE[q.dtype], _stream(dev))
     _check(st)
     return (out, lse) if return_lse else out
 
@@ -267,7 +306,7 @@ def attn_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torch.Tenso
     return dq, dk, dv
 
 
-__all__ = ["attn_fwd", "attn_decode", "attn_bwd", "bwd_workspace_size", "decode_workspace_size", "decode_num_splits",
+__all__ = ["attn_fwd", "attn_fwd_block_sparse", "SPARSE_BLOCK", "attn_decode", "attn_bwd", "bwd_workspace_size", "decode_workspace_size", "decode_num_splits",
            "decode_workspace", "lib", "last_error", "status_string", "SaAttnError",
            "SIGNATURES", "LIB_PATH", "SA_OK", "SA_ERR_INVALID_ARG", "SA_ERR_UNSUPPORTED",
            "SA_ERR_WORKSPACE", "SA_ERR_HIP", "SA_F16", "SA_BF16"]

@@ -58,17 +58,19 @@ def build(verbose: bool = False) -> Path:
     host_o = BUILD / "host_logic.o"
     dev_o = BUILD / "sa_attn.o"
     bwd_o = BUILD / "sa_attn_bwd.o"
-    for p in (host_o, dev_o, bwd_o):
+    sparse_o = BUILD / "sa_attn_sparse.o"
+    for p in (host_o, dev_o, bwd_o, sparse_o):
         if p.exists():
             p.unlink()
     steps = [["g++", "-O2", "-std=c++17", "-fPIC", "-Wall", "-c", CSRC / "host_logic.cpp", "-o", host_o],
              [hipcc, *HIP_FLAGS, "-c", CSRC / "sa_attn.hip", "-o", dev_o],
-             [hipcc, *HIP_FLAGS, *BWD_FLAGS, "-c", CSRC / "sa_attn_bwd.hip", "-o", bwd_o]]
+             [hipcc, *HIP_FLAGS, *BWD_FLAGS, "-c", CSRC / "sa_attn_bwd.hip", "-o", bwd_o],
+             [hipcc, *HIP_FLAGS, "-c", CSRC / "sa_attn_sparse.hip", "-o", sparse_o]]
     with ThreadPoolExecutor(len(steps)) as pool:
         for f in [pool.submit(_run, cmd, verbose) for cmd in steps]:
             f.result()
     tmp = LIB.with_suffix(".so.tmp")
-    _run([hipcc, "-shared", f"--offload-arch={ARCH}", "-o", tmp, dev_o, bwd_o, host_o], verbose)
+    _run([hipcc, "-shared", f"--offload-arch={ARCH}", "-o", tmp, dev_o, bwd_o, sparse_o, host_o], verbose)
     os.replace(tmp, LIB)
     return LIB
 

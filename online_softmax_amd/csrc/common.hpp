@@ -93,6 +93,10 @@ __device__ inline float sum_quarters(float x) {
 
 // True in every lane when the predicate holds in any lane of the wave.
 __device__ inline bool wave_any(bool p) { return __builtin_amdgcn_ballot_w64(p) != 0; }
+// Number of set bits of a wave mask in the lanes below `lane`.
+__device__ inline int lanes_below(uint64_t m, int lane) {
+  return __builtin_popcountll(m & ((uint64_t(1) << lane) - 1));
+}
 
 // Transposing LDS read: in every group of 16 lanes, lane t supplies the
 // address of four consecutive 16-bit words; lane u receives word (u % 4) of

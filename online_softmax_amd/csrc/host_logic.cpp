@@ -108,6 +108,24 @@ int check_fwd(const FwdShape& s, bool* noop) {
   return SA_OK;
 }
 
+int check_block_sparse(const FwdShape& s, const uint8_t* block_mask, bool* noop) {
+  int st = check_fwd(s, noop);
+  if (st != SA_OK || *noop) return st;
+  if (s.S_k > 64 * kSparseMaxTiles)
+    return fail(SA_ERR_UNSUPPORTED, "block-sparse forward supports S_k up to %d (got %d)",
+                64 * kSparseMaxTiles, s.S_k);
+  if (s.S_k == 0) return SA_OK;  // no keys: the block mask is not read
+  if (!block_mask) return fail(SA_ERR_INVALID_ARG, "block_mask must not be NULL when S_k > 0");
+  int64_t nb = 1;
+  if (!mul_ok(&nb, s.B) || !mul_ok(&nb, s.H_q) || !mul_ok(&nb, (s.S_q + kSparseBlock - 1) / kSparseBlock) ||
+      !mul_ok(&nb, (s.S_k + kSparseBlock - 1) / kSparseBlock))
+    return fail(SA_ERR_INVALID_ARG, "block mask size overflows");
+  const size_t qb = (size_t)s.B * s.S_q * s.H_q * s.D * 2, lb = (size_t)s.B * s.H_q * s.S_q * 4;
+  if (overlap(s.out, qb, block_mask, (size_t)nb) || overlap(s.lse, s.lse ? lb : 0, block_mask, (size_t)nb))
+    return fail(SA_ERR_INVALID_ARG, "out/lse overlap the block mask");
+  return SA_OK;
+}
+
 int decode_num_splits(int B, int S_k, int H_q, int H_kv, int num_cu) {
   if (B <= 0 || S_k <= 0 || H_q <= 0 || H_kv <= 0 || H_q % H_kv) return 1;
   const int G = H_q / H_kv;

@@ -38,6 +38,12 @@ constexpr int kDecodeHeadGroup = 16;
 // 32 keys); the last round of a split may run past its end.
 constexpr int kDecodeRoundKeys = 512;
 
+// Block-sparse prefill: block size for query rows and keys (the default
+// attention block of the "Stem" page, section 6), and the capacity of a
+// workgroup's list of 64-key tiles, which bounds S_k at 64 * kSparseMaxTiles.
+constexpr int kSparseBlock = 128;
+constexpr int kSparseMaxTiles = 4096;
+
 // Records a formatted message as the calling thread's last error and returns
 // the status unchanged.
 int fail(int status, const char* fmt, ...);
@@ -50,6 +56,9 @@ const char* status_string(int status);
 int check_fwd(const FwdShape& s, bool* noop);
 int check_decode(const DecodeShape& s, bool* noop);
 int check_bwd(const BwdShape& s, bool* noop);
+// The forward's checks plus those of the block mask
+// [B, H_q, ceil(S_q / kSparseBlock), ceil(S_k / kSparseBlock)].
+int check_block_sparse(const FwdShape& s, const uint8_t* block_mask, bool* noop);
 // Bytes of backward workspace: one float2 {lse in base 2, row dot} per
 // (batch, query head, row); 0 for a negative size or on overflow.
 size_t bwd_workspace_size(int B, int H_q, int S_q);

@@ -39,6 +39,12 @@
 //    masking pass; tiles on the causal diagonal, at the ragged end of the
 //    keys or with padded keys take it.  Which tiles are free of padding is
 //    worked out once per workgroup into a bit per tile;
+//  * block-sparse mode (the execution step of the "Stem: Rethinking Causal
+//    Information Flow in Sparse Attention" page, section 2.3): a workgroup
+//    of 4 waves owns one block of 128 query rows and sweeps only the key
+//    blocks of 128 that its row of the block mask selects; wave 0 compacts
+//    the selected 64-key tiles into a list in LDS, and the sweep walks that
+//    list in key order with everything else unchanged;
 //  * the reference maximum is raised only when a tile's maximum exceeds it by
 //    more than kRescaleSlack (base 2): the final out = numerator / denominator
 //    and lse = reference + log(denominator) are exact for any reference, and
@@ -46,6 +52,7 @@
 //    rescaling the output accumulator.
 #pragma once
 #include "common.hpp"
+#include "host_logic.hpp"
 
 namespace sa {
 
@@ -67,6 +74,8 @@ struct FwdArgs {
   float alibi2;  // log2(e) / |scale log2(e)| = 1 / |scale|: bias to accumulator units
   int nmb;       // query blocks per (batch, head)
   int nitems;    // B * H_q * nmb
+  const uint8_t* block_mask;  // block-sparse mode: [B, H_q, nmb, nkb], nonzero = visit
+  int nkb;                    // key blocks of kSparseBlock per row of block_mask
 };
 
 // Chunk swizzle of LDS row r (16-byte chunks, D / 8 per row).
@@ -76,7 +85,7 @@ __device__ inline int lds_swizzle(int r) {
   else return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);
 }
 
-template <class T, int D, bool CAUSAL, bool MASK, bool ALIBI, int NW>
+template <class T, int D, bool CAUSAL, bool MASK, bool ALIBI, int NW, bool SPARSE = false>
 __global__ __launch_bounds__(NW * 64, 2) void fwd_kernel(FwdArgs a) {
   constexpr int BM = 32 * NW;        // query rows per workgroup
   constexpr int BN = 64;             // keys per tile
@@ -85,10 +94,13 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_kernel(FwdArgs a) {
   constexpr int DB = D / 32;         // 32-row blocks of O^T
   constexpr int NI = BN * D * 2 / 1024 / NW;  // 1 KiB copies per wave per tensor per tile
   static_assert(NI >= 1, "tile too small for the copy layout");
+  static_assert(!SPARSE || BM == kSparseBlock, "a block-sparse workgroup owns one query block");
 
   __shared__ __attribute__((aligned(1024))) uint16_t Ks[NS][BN * D];
   __shared__ __attribute__((aligned(1024))) uint16_t Vs[NS][BN * D];
   __shared__ uint32_t Mf[MASK ? kMaskFlagTiles / 32 : 1];
+  __shared__ int16_t Tl[SPARSE ? kSparseMaxTiles : 1];  // block-sparse tile list
+  __shared__ int Tn;                                     // its length
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -106,7 +118,32 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_kernel(FwdArgs a) {
 
   int n_end = a.S_k;
   if (CAUSAL) n_end = min(n_end, m0 + BM + off);
-  const int nt = n_end > 0 ? (n_end + BN - 1) / BN : 0;
+  const int ntd = n_end > 0 ? (n_end + BN - 1) / BN : 0;  // tiles up to the last key any row may see
+  int nt = ntd;                                           // tiles the sweep visits
+
+  // Block-sparse mode: the selected tiles of this query block in key order.
+  // Wave 0 takes 64 key blocks per round, one per lane; a selected block
+  // contributes its one or two tiles below ntd, placed by two ballots.
+  if constexpr (SPARSE) {
+    if (w == 0) {
+      const uint8_t* brow = a.block_mask + ((size_t)bh * a.nmb + mb) * a.nkb;
+      const int nkv = (ntd + 1) / 2;  // key blocks holding a tile below ntd
+      int base = 0;
+      for (int kb0 = 0; kb0 < nkv; kb0 += 64) {
+        const int kbl = kb0 + lane;
+        const bool sel = kbl < nkv && brow[kbl < nkv ? kbl : 0] != 0;
+        const bool two = sel && 2 * kbl + 1 < ntd;
+        const uint64_t bs = __builtin_amdgcn_ballot_w64(sel), bt = __builtin_amdgcn_ballot_w64(two);
+        const int pos = base + lanes_below(bs, lane) + lanes_below(bt, lane);
+        if (sel) Tl[pos] = (int16_t)(2 * kbl);
+        if (two) Tl[pos + 1] = (int16_t)(2 * kbl + 1);
+        base += __builtin_popcountll(bs) + __builtin_popcountll(bt);
+      }
+      if (lane == 0) Tn = base;
+    }
+    __syncthreads();
+    nt = __builtin_amdgcn_readfirstlane(Tn);
+  }
 
   const size_t rs = (size_t)a.H_kv * D;  // key/value row stride
   const uint16_t* kb = a.k + ((size_t)b * a.S_k * a.H_kv + hk) * D;
@@ -135,9 +172,12 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_kernel(FwdArgs a) {
   // the steeper slopes); and the workgroups of one head still walk the shared
   // tiles from key 0 together, which keeps them in L2.  Otherwise the order
   // is plain 0 .. nt-1.
-  constexpr bool BAND = CAUSAL && ALIBI;
+  constexpr bool BAND = CAUSAL && ALIBI && !SPARSE;
   const int nb = BAND ? min(nt, BM / BN) : 0;
-  auto tile_of = [&](int it) { return it < nb ? nt - 1 - it : it - nb; };
+  auto tile_of = [&](int it) -> int {
+    if constexpr (SPARSE) return __builtin_amdgcn_readfirstlane((int)Tl[it]);
+    else return it < nb ? nt - 1 - it : it - nb;
+  };
   auto issue_k = [&](int t) {
     const auto r = tile_rsrc(kb, tile_of(t) * BN);
     uint16_t* buf = Ks[t % NS];
@@ -183,7 +223,7 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_kernel(FwdArgs a) {
   if (MASK) {
     for (int x = tid; x < kMaskFlagTiles / 32; x += NW * 64) Mf[x] = 0;
     __syncthreads();
-    const int ntf = min(nt, kMaskFlagTiles);
+    const int ntf = min(ntd, kMaskFlagTiles);
     for (int t0 = 16 * w; t0 < ntf; t0 += 16 * NW) {
       const int j0 = (t0 + (lane >> 2)) * BN + 16 * (lane & 3);
       bool keep = true;
@@ -459,7 +499,23 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_kernel(FwdArgs a) {
   // the last ntw (the band tiles past the wave's diagonal come first and are
   // the ones it skips).
   int ntw = wave_active ? nt : 0;
-  if (CAUSAL) ntw = wave_last < 0 ? 0 : min(ntw, wave_last / BN + 1);
+  if (CAUSAL) {
+    if (wave_last < 0) {
+      ntw = 0;
+    } else if constexpr (SPARSE) {
+      // Entries of the (ascending) list at or before the wave's last tile.
+      const int last_tile = wave_last / BN;
+      int lo = 0, hi = ntw;
+      while (lo < hi) {
+        const int mid = (lo + hi) >> 1;
+        if (tile_of(mid) <= last_tile) lo = mid + 1;
+        else hi = mid;
+      }
+      ntw = lo;
+    } else {
+      ntw = min(ntw, wave_last / BN + 1);
+    }
+  }
   const int t0w = BAND ? nt - ntw : 0;
   const int t1w = BAND ? nt : ntw;
 

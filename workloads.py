@@ -128,6 +128,31 @@ def make_dout(w: Workload, seed: Optional[int] = None) -> torch.Tensor:
     return torch.randn((w.B, w.S_q, w.H_q, w.D), generator=g).to(DTYPES[w.dtype])
 
 
+def make_block_mask(w: Workload, keep: float = 0.2, sinks: int = 4, window: int = 4,
+                    seed: Optional[int] = None, block: int = 128) -> torch.Tensor:
+    """Seeded block selection for the block-sparse forward, shaped like the
+    selections of the "Stem" page: per (batch, query head, query block x),
+    the first ``sinks`` key blocks and the ``window`` key blocks ending at the
+    query block's own diagonal (its section 6 defaults ``initial_blocks`` = 4
+    and ``window_size`` = 4) are always selected, and every other key block
+    independently with probability ``keep`` (standing in for the top-k of
+    its scores).  The diagonal of block x is the key block holding key
+    ``x * block + block - 1 + S_k - S_q`` (bottom-right alignment).
+    Returns uint8 ``[B, H_q, ceil(S_q / block), ceil(S_k / block)]``.
+    """
+    g = torch.Generator().manual_seed(w.seed + 2000 if seed is None else seed)
+    nbq, nbk = -(-w.S_q // block), -(-w.S_k // block)
+    bm = (torch.rand((w.B, w.H_q, nbq, nbk), generator=g) < keep).to(torch.uint8)
+    bm[:, :, :, :min(sinks, nbk)] = 1
+    for x in range(nbq):
+        last = min(x * block + block - 1 + w.S_k - w.S_q, w.S_k - 1)
+        if last < 0:
+            continue
+        d = last // block
+        bm[:, :, x, max(0, d - window + 1):d + 1] = 1
+    return bm
+
+
 def to_f64(t: torch.Tensor) -> np.ndarray:
     """Exact float64 numpy copy of a CPU tensor (fp16/bf16 values are exact in fp64)."""
     return t.detach().to("cpu", torch.float64).numpy()
