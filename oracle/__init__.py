@@ -21,6 +21,10 @@ fast:
   key block) pairs, the execution step of the "Stem" page (section 2.3),
   written as its pseudo-sparse fallback: the block selection expanded into an
   element mask, then the definition above.
+* ``attention_ext`` — ``attention`` with an additive float mask and dropout
+  by a Philox4x32-10 rule ("StreamAttention" page, "Recent Updates" and
+  "API Reference"); the generator is ``philox``, written from its published
+  definition.
 * ``merge_states`` — the log-sum-exp weighted combination of partial states
   ("StreamAttention" page, "Engine Direction" and "Distributed and
   Long-Context Variants").
@@ -30,11 +34,12 @@ Every function here is pinned by tests that do not go through the oracle's own
 code path (closed forms, invariants, a library routine, brute force); none of
 them is "parity unpinned".
 """
-from .attention import (SPARSE_BLOCK, attention, attention_bwd, attention_probs,
+from .attention import (SPARSE_BLOCK, attention, attention_bwd, attention_ext, attention_probs,
                         block_sparse_attention, online_attention, merge_states, partial_state,
                         alibi_bias, visible)
-from . import brute
+from . import brute, philox
 
-__all__ = ["SPARSE_BLOCK", "attention", "attention_bwd", "attention_probs", "block_sparse_attention",
+__all__ = ["SPARSE_BLOCK", "attention", "attention_bwd", "attention_ext", "attention_probs",
+           "block_sparse_attention", "philox",
            "online_attention", "merge_states",
            "partial_state", "alibi_bias", "visible", "brute"]

@@ -39,6 +39,8 @@ from __future__ import annotations
 
 import numpy as np
 
+from . import philox
+
 
 def _f64(x):
     return np.asarray(x, dtype=np.float64)
@@ -123,6 +125,54 @@ def attention(q, k, v, scale, causal=False, key_padding_mask=None,
                 bias = alibi_bias(np.asarray(alibi_slopes, np.float64)[h], S_q, S_k, rows)
             s = _scores(q[b, rows, h, :], k[b, :, hk, :], scale, keep, bias)
             P, lse[b, h] = _softmax_rows(s)
+            out[b, :, h, :] = P @ v[b, :, hk, :]
+    return out, lse
+
+
+def attention_ext(q, k, v, scale, causal=False, key_padding_mask=None, alibi_slopes=None,
+                  attn_bias=None, dropout_p=0.0, seed=0, offset=0, rows=None):
+    """``attention`` with an additive float mask and dropout.
+
+    The forward of the "StreamAttention" page with its additive masks and
+    deterministic Philox dropout ("Recent Updates"; ``attention_mask`` and
+    ``dropout_p`` of ``forward`` in "API Reference"):
+
+    * ``attn_bias`` (broadcastable to ``[B, H_q, S_q, S_k]``) is added to the
+      scaled scores next to the ALiBi bias; ``-inf`` hides a key;
+    * the softmax, and so ``lse``, is that of the scores before dropout;
+    * with ``dropout_p > 0`` each probability is kept or zeroed by the Philox
+      rule of ``oracle.philox.keep_mask`` and the kept ones are divided by
+      ``1 - dropout_p``, so ``out_i = sum_j P[i, j] keep[i, j] v_j / (1 - p)``.
+
+    Returns ``out [B, R, H_q, D]`` and ``lse [B, H_q, R]`` in float64.
+    """
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    B, S_q, H_q, D = q.shape
+    S_k, H_kv = k.shape[1], k.shape[2]
+    if H_q % H_kv:
+        raise ValueError("H_q must be a multiple of H_kv")
+    G = H_q // H_kv
+    rows = np.arange(S_q) if rows is None else np.asarray(rows, dtype=np.int64)
+    R = len(rows)
+    ab = None if attn_bias is None else np.broadcast_to(_f64(attn_bias), (B, H_q, S_q, S_k))
+    p = float(dropout_p)
+    philox.drop_threshold(p)  # validates p
+    out = np.zeros((B, R, H_q, D))
+    lse = np.full((B, H_q, R), -np.inf)
+    for b in range(B):
+        mrow = None if key_padding_mask is None else np.asarray(key_padding_mask)[b]
+        keep = visible(S_q, S_k, causal, mrow, rows)
+        for h in range(H_q):
+            hk = h // G
+            bias = np.zeros((R, S_k))
+            if alibi_slopes is not None:
+                bias = bias + alibi_bias(np.asarray(alibi_slopes, np.float64)[h], S_q, S_k, rows)
+            if ab is not None:
+                bias = bias + ab[b, h][rows]
+            s = _scores(q[b, rows, h, :], k[b, :, hk, :], scale, keep, bias)
+            P, lse[b, h] = _softmax_rows(s)
+            if p > 0.0:
+                P = P * philox.keep_mask(b, h, H_q, rows, S_k, p, seed, offset) / (1.0 - p)
             out[b, :, h, :] = P @ v[b, :, hk, :]
     return out, lse
 

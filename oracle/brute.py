@@ -11,14 +11,21 @@ from __future__ import annotations
 
 import math
 
+from .philox import drop_threshold, philox4x32_10
+
 
 def attention(q, k, v, scale, causal=False, key_padding_mask=None,
-              alibi_slopes=None, block_mask=None, block=128):
+              alibi_slopes=None, block_mask=None, block=128, attn_bias=None,
+              dropout_p=0.0, seed=0, offset=0):
     """q: nested ``[B][S_q][H_q][D]``; k, v: ``[B][S_k][H_kv][D]``.
 
     ``block_mask`` (nested ``[B][H_q][query block][key block]``, truthy =
     selected) restricts row i to keys whose block of ``block`` keys is
-    selected for the block of ``block`` rows holding i.
+    selected for the block of ``block`` rows holding i.  ``attn_bias``
+    (nested ``[B][H_q][S_q][S_k]``) is added to the scaled score; with
+    ``dropout_p > 0`` each term of the output sum is kept when its Philox word
+    (one generator call per element) reaches the drop threshold, and is then
+    divided by ``1 - dropout_p``.
 
     Returns ``(out [B][S_q][H_q][D], lse [B][H_q][S_q])`` as Python floats.
     """
@@ -45,6 +52,10 @@ def attention(q, k, v, scale, causal=False, key_padding_mask=None,
                     sc = float(scale) * dot
                     if alibi_slopes is not None:
                         sc -= float(alibi_slopes[h]) * abs(pos - j)
+                    if attn_bias is not None:
+                        sc += float(attn_bias[b][h][i][j])
+                        if sc == float("-inf"):
+                            continue
                     keys.append(j)
                     scores.append(sc)
                 if not keys:
@@ -53,8 +64,14 @@ def attention(q, k, v, scale, causal=False, key_padding_mask=None,
                 total = math.fsum(math.exp(x - top) for x in scores)
                 row_lse = top + math.log(total)
                 lse[b][h][i] = row_lse
+                weight = [math.exp(sc - row_lse) for sc in scores]
+                if dropout_p > 0.0:
+                    thr = drop_threshold(dropout_p)
+                    for n, j in enumerate(keys):
+                        word = philox4x32_10((j // 4, i, b * H_q + h, offset),
+                                             (seed & 0xFFFFFFFF, seed >> 32))[j % 4]
+                        weight[n] = weight[n] / (1.0 - dropout_p) if word >= thr else 0.0
                 for d in range(D):
                     out[b][i][h][d] = math.fsum(
-                        math.exp(sc - row_lse) * float(v[b][j][hk][d])
-                        for sc, j in zip(scores, keys))
+                        wt * float(v[b][j][hk][d]) for wt, j in zip(weight, keys))
     return out, lse
