@@ -27,6 +27,10 @@ The ``*_sparse`` workload times the block-sparse forward
 window, 20 % of the rest); its FLOPs count only the visible pairs of the
 selected blocks.
 
+The ``*_ext`` workload times the extended forward (``sa_attn_fwd_ext``) with
+a seeded [B, 1, S_q, S_k] float32 bias and dropout 0.1; its FLOPs are the
+forward's (a bias entry of -inf still costs its score).
+
 The ``*_bwd`` workloads time the backward instead (``sa_attn_bwd``: the
 per-row pre-pass, the dq kernel and the dk/dv kernel) on the same inputs,
 with ``out`` and ``lse`` from one forward call made before timing.  Their
@@ -72,6 +76,7 @@ STEPS = {
     "c2_causal_pad16": ["c2_causal_pad16"],
     "c1_fwd_256": ["c1_fwd_256"],
     "c5_alibi_8192_sparse": ["c5_alibi_8192:sparse"],
+    "c3_causal_4096_ext": ["c3_causal_4096:ext"],
     "c3_causal_4096_bwd": ["c3_causal_4096:bwd"],
     "c5_alibi_8192_bwd": ["c5_alibi_8192:bwd"],
 }
@@ -155,10 +160,11 @@ class Part:
     def __init__(self, name, dev):
         import torch
         import online_softmax_amd as sa
-        from workloads import WORKLOADS, make_block_mask, make_dout, make_inputs
+        from workloads import WORKLOADS, make_bias, make_block_mask, make_dout, make_inputs
         name, _, mode = name.partition(":")
         self.bwd = mode == "bwd"
         self.sparse = mode == "sparse"
+        self.ext = mode == "ext"
         self.w = w = WORKLOADS[name]
         self.sa = sa
         inp = make_inputs(w)
@@ -176,6 +182,10 @@ class Part:
         self.out = torch.empty_like(self.q)
         self.flops = algorithmic_flops(w, self.tails, self.bwd)
         self.calls = 0
+        if self.ext:
+            self.bias_cpu = make_bias(w, "b1qk")
+            self.bias = d(self.bias_cpu)
+            self.dropout_p, self.seed = 0.1, 2024
         if self.sparse:
             self.bm_cpu = make_block_mask(w)
             self.bm = d(self.bm_cpu)
@@ -199,6 +209,11 @@ class Part:
                              causal=w.causal, scale=w.scale, key_padding_mask=self.mask,
                              alibi_slopes=self.slopes, dq=self.dq, dk=self.dk, dv=self.dv,
                              workspace=self.ws)
+        elif self.ext:
+            self.sa.attn_fwd_ext(self.q, self.ks[0], self.vs[0], causal=w.causal, scale=w.scale,
+                                 key_padding_mask=self.mask, alibi_slopes=self.slopes,
+                                 attn_bias=self.bias, dropout_p=self.dropout_p, seed=self.seed,
+                                 offset=self.calls, out=self.out, lse=self.lse)
         elif self.sparse:
             self.sa.attn_fwd_block_sparse(self.q, self.ks[0], self.vs[0], self.bm, causal=w.causal,
                                           scale=w.scale, key_padding_mask=self.mask,
@@ -245,6 +260,17 @@ def cpu_baseline(parts, budget_s):
             n = min(n_rows, w.S_q - done_rows)
             rows = (np.arange(done_rows, done_rows + n) * 7919) % w.S_q
             t0 = time.perf_counter()
+            if p.ext:
+                oracle.attention_ext(q, k, v, w.scale, causal=causal, key_padding_mask=mask,
+                                     alibi_slopes=sl, attn_bias=p.bias_cpu.double().numpy(),
+                                     dropout_p=p.dropout_p, seed=p.seed, rows=rows)
+                used += time.perf_counter() - t0
+                flops += 4 * w.D * w.H_q * sum(int(np.clip(np.minimum(
+                    rows + (w.S_k - w.S_q) if causal else np.full(len(rows), w.S_k - 1),
+                    w.S_k - 1 - (inp.tails[b] if inp.tails else 0)) + 1, 0, None).sum()) for b in range(w.B))
+                done_rows += n
+                n_rows *= 2
+                continue
             if p.sparse:
                 oracle.block_sparse_attention(q, k, v, w.scale, p.bm_cpu.numpy(), causal=causal,
                                               key_padding_mask=mask, alibi_slopes=sl, rows=rows)
@@ -397,6 +423,7 @@ def main():
         "data": "synthetic (seeded N(0,1) q/k/v)",
         "config": {"workload": args.workload,
                    "parts": [f"{p.w.name}{' backward' if p.bwd else ''}"
+                             f"{' + [B,1,S_q,S_k] float bias + dropout %.1f' % p.dropout_p if p.ext else ''}"
                              f"{' block-sparse (%.1f %% of blocks selected)' % (100 * p.bm_cpu.float().mean().item()) if p.sparse else ''}: B={p.w.B} S_q={p.w.S_q} S_k={p.w.S_k} H_q={p.w.H_q} "
                              f"H_kv={p.w.H_kv} D={p.w.D} {p.w.dtype} causal={p.w.causal} "
                              f"mask={'tails ' + str(p.tails) if p.tails else 'none'} "
@@ -422,8 +449,10 @@ def main():
         result["roofline"] = {"bound": "mfma", "achieved": round(ach, 2), "peak": MFMA_PEAK_TFLOPS,
                               "unit": "TFLOP/s", "frac": round(ach / MFMA_PEAK_TFLOPS, 4),
                               "traffic": read_traffic("fwd_kernel", p.w.name),
-                              "kernel": "fwd_kernel" + (" (block-sparse)" if p.sparse else ""),
-                              "workload": p.w.name + (" block-sparse" if p.sparse else ""),
+                              "kernel": "fwd_kernel" + (" (block-sparse)" if p.sparse else "")
+                                        + (" (bias + dropout)" if p.ext else ""),
+                              "workload": p.w.name + (" block-sparse" if p.sparse else "")
+                                          + (" bias + dropout" if p.ext else ""),
                               "avg_launch_ms": round(t, 4), "flops_per_launch": p.flops,
                               "dense_count_tflops": round(4 * p.w.B * p.w.H_q * p.w.S_q * p.w.S_k * p.w.D
                                                           / (t * 1e-3) / 1e12, 2)}

@@ -111,6 +111,42 @@ int sa_attn_fwd_block_sparse(const void* q, const void* k, const void* v, void* 
                              sa_stream_t stream);
 
 /*
+ * Attention forward with an additive float mask and dropout ("StreamAttention:
+ * Fused Online Softmax Attention" page, "Recent Updates": boolean/additive
+ * masks, dropout and deterministic Philox seeding; "API Reference":
+ * attention_mask and dropout_p).  Arguments and rules as in sa_attn_fwd,
+ * plus:
+ *
+ *   attn_bias  float32, device, or NULL: element (b, h, i, j) at
+ *              attn_bias[b * bias_stride_b + h * bias_stride_h
+ *                        + i * bias_stride_q + j],
+ *              added to the scaled score of query row i and key j next to
+ *              the ALiBi bias; -inf hides the key.  Strides are in elements,
+ *              non-negative multiples of 4 (0 broadcasts that axis); the
+ *              pointer is 16-byte aligned.  Entries must not be +inf or NaN.
+ *   dropout_p  in [0, 1); 0 turns dropout off.  A probability P[i, j] of
+ *              (batch b, query head h) is kept when word (j mod 4) of
+ *              Philox4x32-10 (Salmon et al., SC'11) with counter
+ *              (j / 4, i, b * H_q + h, offset) and key (seed low word, seed
+ *              high word) is at least floor(dropout_p * 2^32); the output is
+ *              sum_j P[i, j] keep[i, j] v_j / (1 - dropout_p).  lse is that
+ *              of the softmax before dropout.
+ *   seed, offset: the generator's key and fourth counter word (advance
+ *              offset between calls that share a seed).
+ *
+ * Runs workgroups of four waves.  B == 0 or S_q == 0 is a successful no-op.
+ * Errors: SA_ERR_INVALID_ARG (also for a dropout_p outside [0, 1), bad bias
+ * strides or alignment, out/lse overlapping the bias), SA_ERR_UNSUPPORTED,
+ * SA_ERR_HIP.
+ */
+int sa_attn_fwd_ext(const void* q, const void* k, const void* v, void* out, float* lse,
+                    int B, int S_q, int S_k, int H_q, int H_kv, int D, float scale,
+                    int causal, const uint8_t* key_padding_mask, const float* alibi_slopes,
+                    const float* attn_bias, int64_t bias_stride_b, int64_t bias_stride_h,
+                    int64_t bias_stride_q, double dropout_p, uint64_t seed, uint32_t offset,
+                    int dtype, sa_stream_t stream);
+
+/*
  * Bytes of device workspace sa_attn_decode needs for these sizes (an upper
  * bound that holds for every H_kv dividing H_q).  Pure host arithmetic: no
  * HIP call.  Returns 0 when a size is negative or the result would overflow.

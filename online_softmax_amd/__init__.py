@@ -14,6 +14,9 @@ Functions keep the names of the C entry points:
 * ``attn_decode(q, k_cache, v_cache, scale=None, key_padding_mask=None,
   alibi_slopes=None, out=None, lse=None, workspace=None, return_lse=True)``
 * ``decode_workspace_size(B, H_q, S_k, D)`` and ``decode_num_splits(...)``
+* ``attn_fwd_block_sparse(q, k, v, block_mask, causal=False, ...)``
+* ``attn_fwd_ext(q, k, v, causal=False, ..., attn_bias=None, dropout_p=0.0,
+  seed=0, offset=0)``
 * ``attn_bwd(q, k, v, out, dout, lse, causal=False, scale=None, key_padding_mask=None,
   alibi_slopes=None)`` -> ``(dq, dk, dv)`` and ``bwd_workspace_size(B, H_q, S_q)``
 """
@@ -35,10 +38,13 @@ _DTYPE = {torch.float16: SA_F16, torch.bfloat16: SA_BF16}
 # Every symbol the public header declares, with its ctypes signature.
 _VP, _FP, _U8P = ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p
 _I, _F, _SZ = ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+_I64, _D, _U64, _U32 = ctypes.c_int64, ctypes.c_double, ctypes.c_uint64, ctypes.c_uint32
 SIGNATURES = {
     "sa_attn_fwd": (_I, [_VP, _VP, _VP, _VP, _FP, _I, _I, _I, _I, _I, _I, _F, _I, _U8P, _FP, _I, _VP]),
     "sa_attn_fwd_block_sparse": (_I, [_VP, _VP, _VP, _VP, _FP, _I, _I, _I, _I, _I, _I, _F, _I, _U8P, _FP,
                                       _U8P, _I, _VP]),
+    "sa_attn_fwd_ext": (_I, [_VP, _VP, _VP, _VP, _FP, _I, _I, _I, _I, _I, _I, _F, _I, _U8P, _FP,
+                             _FP, _I64, _I64, _I64, _D, _U64, _U32, _I, _VP]),
     "sa_attn_decode_workspace_size": (_SZ, [_I, _I, _I, _I]),
     "sa_attn_decode": (_I, [_VP, _VP, _VP, _VP, _FP, _I, _I, _I, _I, _I, _F, _U8P, _FP, _I, _VP, _SZ, _VP]),
     "sa_attn_decode_num_splits": (_I, [_I, _I, _I, _I, _I]),
@@ -197,6 +203,55 @@ def attn_fwd_block_sparse(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
     return (out, lse) if return_lse else out
 
 
+def attn_fwd_ext(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = False,
+                 scale: Optional[float] = None, key_padding_mask: Optional[torch.Tensor] = None,
+                 alibi_slopes: Optional[torch.Tensor] = None,
+                 attn_bias: Optional[torch.Tensor] = None, dropout_p: float = 0.0, seed: int = 0,
+                 offset: int = 0, out: Optional[torch.Tensor] = None,
+                 lse: Optional[torch.Tensor] = None, return_lse: bool = True):
+    """Forward with an additive float mask and dropout through ``sa_attn_fwd_ext``.
+
+    As ``attn_fwd``, plus ``attn_bias``: a float32 tensor on the same device,
+    broadcastable to ``[B, H_q, S_q, S_k]`` (-inf hides a key); and dropout
+    with probability ``dropout_p``, 64-bit ``seed`` and 32-bit ``offset``.
+    A bias whose row strides are not multiples of 4 elements (or whose key
+    axis is not contiguous) is copied into a padded buffer first.
+    """
+    dev, (B, S_q, S_k, H_q, H_kv, D), mask, out, lse, sc = _fwd_prepare(
+        q, k, v, key_padding_mask, alibi_slopes, out, lse, return_lse, scale)
+    bias, strides = None, (0, 0, 0)
+    if attn_bias is not None:
+        if not isinstance(attn_bias, torch.Tensor) or attn_bias.dtype != torch.float32:
+            raise ValueError("attn_bias must be a float32 tensor")
+        if attn_bias.device != dev:
+            raise ValueError(f"attn_bias is on {attn_bias.device}, expected {dev}")
+        try:
+            bias = attn_bias.expand(B, H_q, S_q, S_k)
+        except RuntimeError as e:
+            raise ValueError(f"attn_bias of shape {tuple(attn_bias.shape)} does not broadcast to "
+                             f"{(B, H_q, S_q, S_k)}") from e
+        st4 = bias.stride()
+        if S_k > 1 and st4[3] != 1 or any(x % 4 for x in st4[:3]) or bias.data_ptr() % 16:
+            # Pad the key axis to a multiple of 4 in a fresh buffer (axes the
+            # caller broadcast stay broadcast).
+            shape = [n if attn_bias.dim() - 4 + ax >= 0 and attn_bias.shape[attn_bias.dim() - 4 + ax] != 1
+                     else 1 for ax, n in enumerate((B, H_q, S_q, S_k))]
+            shape[3] = S_k
+            padded = torch.empty(shape[:3] + [-(-S_k // 4) * 4], dtype=torch.float32, device=dev)
+            padded[..., :S_k] = attn_bias.expand(*shape)
+            bias = padded[..., :S_k].expand(B, H_q, S_q, S_k)
+            st4 = bias.stride()
+        strides = st4[:3]
+    st = lib().sa_attn_fwd_ext(q.data_ptr(), _ptr(k), _ptr(v), out.data_ptr(), _ptr(lse),
+                               B, S_q, S_k, H_q, H_kv, D, sc, int(bool(causal)), _ptr(mask),
+                               _ptr(alibi_slopes), None if bias is None else bias.data_ptr(),
+                               strides[0], strides[1], strides[2], float(dropout_p),
+                               int(seed) & (2 ** 64 - 1), int(offset) & (2 ** 32 - 1),
+                               _DTYPE[q.dtype], _stream(dev))
+    _check(st)
+    return (out, lse) if return_lse else out
+
+
 def decode_workspace_size(B: int, H_q: int, S_k: int, D: int) -> int:
     return int(lib().sa_attn_decode_workspace_size(B, H_q, S_k, D))
 
@@ -306,7 +361,7 @@ def attn_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torch.Tenso
     return dq, dk, dv
 
 
-__all__ = ["attn_fwd", "attn_fwd_block_sparse", "SPARSE_BLOCK", "attn_decode", "attn_bwd", "bwd_workspace_size", "decode_workspace_size", "decode_num_splits",
+__all__ = ["attn_fwd", "attn_fwd_block_sparse", "attn_fwd_ext", "SPARSE_BLOCK", "attn_decode", "attn_bwd", "bwd_workspace_size", "decode_workspace_size", "decode_num_splits",
            "decode_workspace", "lib", "last_error", "status_string", "SaAttnError",
            "SIGNATURES", "LIB_PATH", "SA_OK", "SA_ERR_INVALID_ARG", "SA_ERR_UNSUPPORTED",
            "SA_ERR_WORKSPACE", "SA_ERR_HIP", "SA_F16", "SA_BF16"]

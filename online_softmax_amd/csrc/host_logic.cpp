@@ -126,6 +126,35 @@ int check_block_sparse(const FwdShape& s, const uint8_t* block_mask, bool* noop)
   return SA_OK;
 }
 
+uint32_t drop_threshold(double p) {
+  const double t = std::floor(p * 4294967296.0);
+  return t >= 4294967295.0 ? 0xFFFFFFFFu : t <= 0.0 ? 0u : (uint32_t)t;
+}
+
+int check_ext(const FwdShape& s, const ExtShape& e, bool* noop) {
+  if (!(e.dropout_p >= 0.0 && e.dropout_p < 1.0))
+    return fail(SA_ERR_INVALID_ARG, "dropout_p must be in [0, 1) (got %g)", e.dropout_p);
+  int st = check_fwd(s, noop);
+  if (st != SA_OK || *noop || !e.bias || s.S_k == 0) return st;
+  if (e.sb < 0 || e.sh < 0 || e.sq < 0 || e.sb % 4 || e.sh % 4 || e.sq % 4)
+    return fail(SA_ERR_INVALID_ARG, "bias strides must be non-negative multiples of 4 elements");
+  if (!aligned(e.bias, 16)) return fail(SA_ERR_INVALID_ARG, "attn_bias must be 16-byte aligned");
+  // Elements up to the last one read: (B-1) sb + (H_q-1) sh + (S_q-1) sq + S_k.
+  int64_t ext = s.S_k, t;
+  const int64_t terms[3][2] = {{s.B - 1, e.sb}, {s.H_q - 1, e.sh}, {s.S_q - 1, e.sq}};
+  for (const auto& tm : terms) {
+    t = tm[0];
+    if (!mul_ok(&t, tm[1]) || ext > INT64_MAX - t) return fail(SA_ERR_INVALID_ARG, "bias extent overflows");
+    ext += t;
+  }
+  if (ext > INT64_MAX / 4) return fail(SA_ERR_INVALID_ARG, "bias extent overflows");
+  const size_t bb = (size_t)ext * 4;
+  const size_t qb = (size_t)s.B * s.S_q * s.H_q * s.D * 2, lb = (size_t)s.B * s.H_q * s.S_q * 4;
+  if (overlap(s.out, qb, e.bias, bb) || overlap(s.lse, s.lse ? lb : 0, e.bias, bb))
+    return fail(SA_ERR_INVALID_ARG, "out/lse overlap attn_bias");
+  return SA_OK;
+}
+
 int decode_num_splits(int B, int S_k, int H_q, int H_kv, int num_cu) {
   if (B <= 0 || S_k <= 0 || H_q <= 0 || H_kv <= 0 || H_q % H_kv) return 1;
   const int G = H_q / H_kv;

@@ -56,6 +56,17 @@ const char* status_string(int status);
 int check_fwd(const FwdShape& s, bool* noop);
 int check_decode(const DecodeShape& s, bool* noop);
 int check_bwd(const BwdShape& s, bool* noop);
+// Additive bias and dropout of the extended forward.
+struct ExtShape {
+  const float* bias; int64_t sb, sh, sq;  // element strides; key axis contiguous
+  double dropout_p;
+};
+// The forward's checks plus those of the bias (alignment, strides, extent,
+// overlap with out/lse) and of the dropout probability (0 <= p < 1).
+int check_ext(const FwdShape& s, const ExtShape& e, bool* noop);
+// Words below this 32-bit threshold drop: floor(p * 2^32).
+uint32_t drop_threshold(double p);
+
 // The forward's checks plus those of the block mask
 // [B, H_q, ceil(S_q / kSparseBlock), ceil(S_k / kSparseBlock)].
 int check_block_sparse(const FwdShape& s, const uint8_t* block_mask, bool* noop);

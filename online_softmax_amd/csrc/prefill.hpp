@@ -45,6 +45,12 @@
 //    blocks of 128 that its row of the block mask selects; wave 0 compacts
 //    the selected 64-key tiles into a list in LDS, and the sweep walks that
 //    list in key order with everything else unchanged;
+//  * extended mode (the additive masks and Philox dropout of the
+//    "StreamAttention" page, "Recent Updates"): an additive float32 bias is
+//    loaded for each tile while the previous tile's matrix work runs and is
+//    added to the scores (in accumulator units, like ALiBi) before the
+//    maximum; dropout keeps or zeroes each probability by a Philox4x32-10
+//    word of its (row, key) position, after the row sum has taken it;
 //  * the reference maximum is raised only when a tile's maximum exceeds it by
 //    more than kRescaleSlack (base 2): the final out = numerator / denominator
 //    and lse = reference + log(denominator) are exact for any reference, and
@@ -76,7 +82,42 @@ struct FwdArgs {
   int nitems;    // B * H_q * nmb
   const uint8_t* block_mask;  // block-sparse mode: [B, H_q, nmb, nkb], nonzero = visit
   int nkb;                    // key blocks of kSparseBlock per row of block_mask
+  // Extended mode.  Bias element (b, h, i, j) at bias[b sb + h sh + i sq + j]
+  // (strides in elements, multiples of 4; NULL = none).  Dropout: a
+  // probability is kept when its Philox word is >= drop_thr (0 = no dropout);
+  // kept ones are scaled by drop_scale = 1 / (1 - p) in the epilogue.
+  const float* bias;
+  int64_t bias_sb, bias_sh, bias_sq;
+  uint32_t drop_thr;
+  float drop_scale;
+  uint32_t seed_lo, seed_hi, drop_offset;
 };
+
+// Philox4x32-10 (Salmon, Moraes, Dror and Shaw, "Parallel random numbers: as
+// easy as 1, 2, 3", SC'11): ten rounds over a 128-bit counter with a 64-bit
+// key, the key bumped by the two Weyl constants between rounds.
+__device__ __attribute__((always_inline)) inline u32x4 philox4x32_10(uint32_t c0, uint32_t c1, uint32_t c2, uint32_t c3,
+                                      uint32_t k0, uint32_t k1) {
+  // The whole generator runs in vector registers, its key schedule
+  // recomputed at every call (two adds a round): hoisted as scalars out of
+  // the caller's loop it would hold twenty scalar registers the kernel does
+  // not have to spare.
+  __asm__ volatile("" : "+v"(k0), "+v"(k1));
+#pragma unroll
+  for (int r = 0; r < 10; ++r) {
+    if (r) {
+      k0 += 0x9E3779B9u;
+      k1 += 0xBB67AE85u;
+    }
+    const uint64_t p0 = (uint64_t)0xD2511F53u * c0, p1 = (uint64_t)0xCD9E8D57u * c2;
+    const uint32_t n0 = (uint32_t)(p1 >> 32) ^ c1 ^ k0, n2 = (uint32_t)(p0 >> 32) ^ c3 ^ k1;
+    c1 = (uint32_t)p1;
+    c3 = (uint32_t)p0;
+    c0 = n0;
+    c2 = n2;
+  }
+  return (u32x4){c0, c1, c2, c3};
+}
 
 // Chunk swizzle of LDS row r (16-byte chunks, D / 8 per row).
 template <int D>
@@ -85,8 +126,9 @@ __device__ inline int lds_swizzle(int r) {
   else return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);
 }
 
-template <class T, int D, bool CAUSAL, bool MASK, bool ALIBI, int NW, bool SPARSE = false>
-__global__ __launch_bounds__(NW * 64, 2) void fwd_kernel(FwdArgs a) {
+template <class T, int D, bool CAUSAL, bool MASK, bool ALIBI, int NW, bool SPARSE = false,
+          bool EXT = false>
+__global__ __launch_bounds__(NW * 64, EXT ? 1 : 2) void fwd_kernel(FwdArgs a) {
   constexpr int BM = 32 * NW;        // query rows per workgroup
   constexpr int BN = 64;             // keys per tile
   constexpr int NS = 2;  // LDS buffers per tensor
@@ -95,6 +137,7 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_kernel(FwdArgs a) {
   constexpr int NI = BN * D * 2 / 1024 / NW;  // 1 KiB copies per wave per tensor per tile
   static_assert(NI >= 1, "tile too small for the copy layout");
   static_assert(!SPARSE || BM == kSparseBlock, "a block-sparse workgroup owns one query block");
+  static_assert(!(SPARSE && EXT), "one mode at a time");
 
   __shared__ __attribute__((aligned(1024))) uint16_t Ks[NS][BN * D];
   __shared__ __attribute__((aligned(1024))) uint16_t Vs[NS][BN * D];
@@ -115,6 +158,12 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_kernel(FwdArgs a) {
   const int off = a.S_k - a.S_q;  // bottom-right alignment of the causal rule
   const int qi = m0 + 32 * w + li;
   const int ipos = qi + off;      // this row's position on the key axis
+
+  // Extended mode: this lane's bias row and whether dropout is on.
+  const bool has_bias = EXT && a.bias != nullptr;
+  const bool dropping = EXT && a.drop_thr != 0u;
+  const float* brow_bias =
+      has_bias && qi < a.S_q ? a.bias + b * a.bias_sb + h * a.bias_sh + qi * a.bias_sq : nullptr;
 
   int n_end = a.S_k;
   if (CAUSAL) n_end = min(n_end, m0 + BM + off);
@@ -344,7 +393,56 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_kernel(FwdArgs a) {
       for (int db = 0; db < DB; ++db) o[db] *= alpha;
     }
   };
+  // Extended mode.  Bias of the tile of iteration it, in the layout of the
+  // scores (register r of block jb: key n0 + 32 jb + 8 (r/4) + 4 g + r%4,
+  // four consecutive keys per quarter): eight 16-byte loads per lane, scalar
+  // loads for a quarter that crosses the end of the keys, zeros past it.
+  auto bias_load = [&](const int it, f32x4 (&bv)[8]) {
+    const int n0 = tile_of(it) * BN;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int j0 = n0 + 32 * (u >> 2) + 8 * (u & 3) + 4 * g;
+      if (brow_bias && j0 + 3 < a.S_k) {
+        bv[u] = *(const f32x4*)(brow_bias + j0);
+      } else {
+        f32x4 x = {0.f, 0.f, 0.f, 0.f};
+        if (brow_bias)
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (j0 + e < a.S_k) x[e] = brow_bias[j0 + e];
+        bv[u] = x;
+      }
+    }
+  };
+  // Adds the bias in accumulator units (bias / |scale|, as for ALiBi).
+  auto bias_add = [&](f32x16 (&s)[2], const f32x4 (&bv)[8]) {
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) s[u >> 2][4 * (u & 3) + e] = fmaf(bv[u][e], a.alibi2, s[u >> 2][4 * (u & 3) + e]);
+  };
+  // Dropout keep bits of the tile of iteration it: bit 16 jb + r for register
+  // r of block jb.  One generator block per quarter of four keys, counter
+  // (key / 4, row, b * H_q + h, offset), word key % 4.
+  auto keep_bits = [&](const int it) __attribute__((always_inline)) -> uint32_t {
+    const int n0 = tile_of(it) * BN;
+    uint32_t bits = 0;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int j0 = n0 + 32 * (u >> 2) + 8 * (u & 3) + 4 * g;
+      const u32x4 wd = philox4x32_10((uint32_t)(j0 >> 2), (uint32_t)qi, (uint32_t)bh, a.drop_offset,
+                                     a.seed_lo, a.seed_hi);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) bits |= (wd[e] >= a.drop_thr ? 1u : 0u) << (16 * (u >> 2) + 4 * (u & 3) + e);
+    }
+    return bits;
+  };
   auto prepare = [&](const int it, f32x16 (&s)[2]) {
+    if (has_bias) {
+      f32x4 bv[8];
+      bias_load(it, bv);
+      bias_add(s, bv);
+    }
     if (tile_masked(it)) mask_tile(it, s);
     raise_max(tile_max(s));
   };
@@ -352,7 +450,9 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_kernel(FwdArgs a) {
   // Probabilities of a prepared tile, packed to the input type, and their sum.
   // While a row has seen no visible key its reference is 0, so that no
   // exp(-inf - (-inf)) is formed.
-  auto softmax_exp = [&](const f32x16 (&s)[2], uint32_t (&pk)[2][8]) {
+  // With dropout (keep bits other than all ones) the row sum takes every
+  // probability and the P·V operand only the kept ones.
+  auto softmax_exp = [&](const f32x16 (&s)[2], uint32_t (&pk)[2][8], const uint32_t keep) {
     const float nm = m_ref == kNegInf ? 0.f : -m_ref;
     float ps[2] = {0.f, 0.f};  // two partial sums: shorter dependency chains
 #pragma unroll
@@ -362,7 +462,12 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_kernel(FwdArgs a) {
         const float p0 = fast_exp2(fmaf(s[jb][r], sc2, nm));
         const float p1 = fast_exp2(fmaf(s[jb][r + 1], sc2, nm));
         ps[jb] += p0 + p1;
-        pk[jb][r >> 1] = T::pack2(p0, p1);
+        if constexpr (EXT) {
+          pk[jb][r >> 1] = T::pack2((keep >> (16 * jb + r)) & 1u ? p0 : 0.f,
+                                    (keep >> (16 * jb + r + 1)) & 1u ? p1 : 0.f);
+        } else {
+          pk[jb][r >> 1] = T::pack2(p0, p1);
+        }
       }
     }
     l_run += ps[0] + ps[1];
@@ -422,17 +527,22 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_kernel(FwdArgs a) {
   static_assert(EQ >= 8 && EQ <= 16, "pair split");
   // One pair of probabilities: exponentials, packed to the input type, summed.
   auto exp_pair = [&](const f32x16 (&s)[2], const int pi, const float nm, uint32_t (&pk)[2][8],
-                      float (&ps)[2]) {
+                      float (&ps)[2], const uint32_t keep) {
     const int jb = pi >> 3, r = 2 * (pi & 7);
     const float p0 = fast_exp2(fmaf(s[jb][r], sc2, nm));
     const float p1 = fast_exp2(fmaf(s[jb][r + 1], sc2, nm));
     ps[jb] += p0 + p1;
-    pk[jb][r >> 1] = T::pack2(p0, p1);
+    if constexpr (EXT) {
+      pk[jb][r >> 1] = T::pack2((keep >> (16 * jb + r)) & 1u ? p0 : 0.f,
+                                (keep >> (16 * jb + r + 1)) & 1u ? p1 : 0.f);
+    } else {
+      pk[jb][r >> 1] = T::pack2(p0, p1);
+    }
   };
   // Phase 1: Sᵀ of the tile of iteration t1 (K fragments read four MFMAs
   // ahead) with pairs 0 .. EQ-1 of the current tile s.
   auto qk_exp = [&](const int t1, f32x16 (&sn)[2], const f32x16 (&s)[2], const float nm,
-                    uint32_t (&pk)[2][8], float (&ps)[2]) {
+                    uint32_t (&pk)[2][8], float (&ps)[2], const uint32_t keep) {
     const uint16_t* kbuf = Ks[t1 % NS];
     u32x4 ak[4];
 #pragma unroll
@@ -445,7 +555,7 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_kernel(FwdArgs a) {
       if (i + 4 < NQK) ak[i & 3] = k_frag(kbuf, i + 4);
       if (i == 0) init_scores(t1, 1, sn);
 #pragma unroll
-      for (int pi = i * EQ / NQK; pi < (i + 1) * EQ / NQK; ++pi) exp_pair(s, pi, nm, pk, ps);
+      for (int pi = i * EQ / NQK; pi < (i + 1) * EQ / NQK; ++pi) exp_pair(s, pi, nm, pk, ps, keep);
       __builtin_amdgcn_sched_barrier(0);
     }
   };
@@ -453,7 +563,7 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_kernel(FwdArgs a) {
   // MFMAs ahead) with pairs EQ .. 15 under its first MFMAs, and the row
   // maximum of the next tile sn (as if no key were hidden) in two chains.
   auto pv_max = [&](const int t, const f32x16 (&s)[2], const float nm, uint32_t (&pk)[2][8],
-                    float (&ps)[2], const f32x16 (&sn)[2]) -> float {
+                    float (&ps)[2], const f32x16 (&sn)[2], const uint32_t keep) -> float {
     const uint16_t* vbuf = Vs[t % NS];
     auto v_frag = [&](const int i) -> u32x4 {
       const int ks = i / DB, db = i % DB;
@@ -477,7 +587,7 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_kernel(FwdArgs a) {
       if (i < H) {
 #pragma unroll
         for (int pi = EQ + i * (16 - EQ) / H; pi < EQ + (i + 1) * (16 - EQ) / H; ++pi)
-          exp_pair(s, pi, nm, pk, ps);
+          exp_pair(s, pi, nm, pk, ps, keep);
       }
 #pragma unroll
       for (int e = 0; e < 32 / NPV; e += 2) {
@@ -549,19 +659,24 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_kernel(FwdArgs a) {
   // masks them and takes it again.  With ALiBi the step runs in the fixed
   // order above; otherwise the scheduler places the same work after the
   // pattern of interleave_schedule, which measured faster there.
-  auto full_step = [&](const int t, f32x16 (&s)[2], f32x16 (&sn)[2]) {
+  // `keep` holds the dropout bits of tile t (all ones without dropout).
+  auto full_step = [&](const int t, f32x16 (&s)[2], f32x16 (&sn)[2], const uint32_t keep) {
     const int n = copies(t);
     uint32_t pk[2][8];
     float tmax;
+    // Extended mode: the next tile's bias is loaded under this step's matrix
+    // work.
+    f32x4 bvn[8];
+    if (has_bias) bias_load(t + 1, bvn);
     if constexpr (ALIBI) {
       float ps[2] = {0.f, 0.f};
       const float nm = m_ref == kNegInf ? 0.f : -m_ref;
-      qk_exp(t + 1, sn, s, nm, pk, ps);
-      tmax = pv_max(t, s, nm, pk, ps, sn);
+      qk_exp(t + 1, sn, s, nm, pk, ps, keep);
+      tmax = pv_max(t, s, nm, pk, ps, sn, keep);
       l_run += ps[0] + ps[1];
     } else {
       qk(t + 1, sn);
-      softmax_exp(s, pk);
+      softmax_exp(s, pk, keep);
       pv(t, pk);
       tmax = tile_max(sn);
       interleave_schedule();
@@ -569,18 +684,24 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_kernel(FwdArgs a) {
       // compiler would otherwise sink it past the masking branch).
       __asm__ volatile("" : "+v"(l_run));
     }
+    bool remax = false;
+    if (has_bias) {
+      bias_add(sn, bvn);
+      remax = true;
+    }
     if (tile_masked(t + 1)) {
       mask_tile(t + 1, sn);
-      tmax = tile_max(sn);
+      remax = true;
     }
+    if (remax) tmax = tile_max(sn);
     raise_max(tmax);
     finish(n);
   };
   // The wave's last tile: probabilities and P·V only.
-  auto last_step = [&](const int t, f32x16 (&s)[2]) {
+  auto last_step = [&](const int t, f32x16 (&s)[2], const uint32_t keep) {
     const int n = copies(t);
     uint32_t pk[2][8];
-    softmax_exp(s, pk);
+    softmax_exp(s, pk, keep);
     pv(t, pk);
     finish(n);
   };
@@ -610,16 +731,21 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_kernel(FwdArgs a) {
       finish(n);
     }
   }
+  // Dropout bits of the tile of iteration it (formed outside the steps, which
+  // stay small enough to be inlined).
+  auto keep_of = [&](const int it) __attribute__((always_inline)) -> uint32_t {
+    return dropping ? keep_bits(it) : ~0u;
+  };
   if (ntw > 0) {
     for (; t + 2 < t1w; t += 2) {
-      full_step(t, sa, sb);
-      full_step(t + 1, sb, sa);
+      full_step(t, sa, sb, keep_of(t));
+      full_step(t + 1, sb, sa, keep_of(t + 1));
     }
     if (t + 1 < t1w) {
-      full_step(t, sa, sb);
-      last_step(t + 1, sb);
+      full_step(t, sa, sb, keep_of(t));
+      last_step(t + 1, sb, keep_of(t + 1));
     } else {
-      last_step(t, sa);
+      last_step(t, sa, keep_of(t));
     }
     t = t1w;
   }
@@ -629,7 +755,8 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_kernel(FwdArgs a) {
   // Epilogue: out = O / l (0 for a row that saw no key), lse = ln of the sum.
   const float l_tot = sum_halves(l_run);
   if (qvalid) {
-    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+    float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+    if (dropping) inv *= a.drop_scale;
     uint16_t* op = a.out + ((size_t)(b * (size_t)a.S_q + qi) * a.H_q + h) * D + 4 * g;
 #pragma unroll
     for (int db = 0; db < DB; ++db) {

@@ -153,6 +153,20 @@ def make_block_mask(w: Workload, keep: float = 0.2, sinks: int = 4, window: int 
     return bm
 
 
+def make_bias(w: Workload, kind: str = "b1qk", ninf: float = 0.02, seed: Optional[int] = None) -> torch.Tensor:
+    """Seeded additive float32 mask: N(0, 1) entries with a fraction ``ninf``
+    set to -inf (hidden keys), at one of the broadcast shapes a caller may
+    pass: ``bhqk`` [B, H_q, S_q, S_k], ``b1qk`` [B, 1, S_q, S_k], ``qk``
+    [S_q, S_k] or ``b11k`` [B, 1, 1, S_k]."""
+    g = torch.Generator().manual_seed(w.seed + 3000 if seed is None else seed)
+    shape = {"bhqk": (w.B, w.H_q, w.S_q, w.S_k), "b1qk": (w.B, 1, w.S_q, w.S_k),
+             "qk": (w.S_q, w.S_k), "b11k": (w.B, 1, 1, w.S_k)}[kind]
+    bias = torch.randn(shape, generator=g)
+    if ninf > 0:
+        bias[torch.rand(shape, generator=g) < ninf] = float("-inf")
+    return bias
+
+
 def to_f64(t: torch.Tensor) -> np.ndarray:
     """Exact float64 numpy copy of a CPU tensor (fp16/bf16 values are exact in fp64)."""
     return t.detach().to("cpu", torch.float64).numpy()
