@@ -58,7 +58,9 @@ sys.path.insert(0, str(ROOT))
 METRIC = "prefill fwd TFLOP/s + decode KV HBM GB/s, each as % of MI355X roofline"
 MFMA_PEAK_TFLOPS = 2500.0   # MI355X dense fp16/bf16 matrix peak (published)
 HBM_PEAK_GBS = 8000.0       # MI355X HBM3E bandwidth (published)
-DECODE_ROTATION = 8
+# Decode steps rotate over copies of the cache totalling at least this many
+# bytes (three times the 256 MB last-level cache), and at least 8 copies.
+DECODE_ROTATION_BYTES = 768 << 20
 PROFILES = ROOT / "profiles"
 # Sources each kernel is built from: a traffic figure measured on other sources is stale.
 KERNEL_SOURCES = {
@@ -73,6 +75,11 @@ STEPS = {
     "c3_noncausal_4096": ["c3_noncausal_4096"],
     "c5_alibi_8192": ["c5_alibi_8192"],
     "c4_decode_32k": ["c4_decode_32k"],
+    "c4_decode_32k_fused": ["c4_decode_32k:fused"],
+    "decode_32k_b1": ["decode_32k_b1"],
+    "decode_32k_b1_fused": ["decode_32k_b1:fused"],
+    "decode_32k_b2": ["decode_32k_b2"],
+    "decode_32k_b2_fused": ["decode_32k_b2:fused"],
     "c2_causal_pad16": ["c2_causal_pad16"],
     "c1_fwd_256": ["c1_fwd_256"],
     "c5_alibi_8192_sparse": ["c5_alibi_8192:sparse"],
@@ -165,6 +172,7 @@ class Part:
         self.bwd = mode == "bwd"
         self.sparse = mode == "sparse"
         self.ext = mode == "ext"
+        self.fused = mode == "fused"
         self.w = w = WORKLOADS[name]
         self.sa = sa
         inp = make_inputs(w)
@@ -172,9 +180,11 @@ class Part:
         d = lambda t: None if t is None else t.to(dev)
         self.q, self.mask, self.slopes = d(inp.q), d(inp.mask), d(inp.slopes)
         if w.decode:
-            self.ks = [d(inp.k)] + [d(inp.k).clone() for _ in range(DECODE_ROTATION - 1)]
-            self.vs = [d(inp.v)] + [d(inp.v).clone() for _ in range(DECODE_ROTATION - 1)]
-            self.ws = sa.decode_workspace(w.B, w.H_q, w.S_k, w.D, dev)
+            n_rot = max(8, -(-DECODE_ROTATION_BYTES // kv_bytes(w)))
+            self.ks = [d(inp.k)] + [d(inp.k).clone() for _ in range(n_rot - 1)]
+            self.vs = [d(inp.v)] + [d(inp.v).clone() for _ in range(n_rot - 1)]
+            self.ws = (sa.decode_fused_workspace if self.fused else sa.decode_workspace)(
+                w.B, w.H_q, w.S_k, w.D, dev)
             self.lse = torch.empty((w.B, w.H_q, 1), dtype=torch.float32, device=dev)
         else:
             self.ks, self.vs = [d(inp.k)], [d(inp.v)]
@@ -218,6 +228,10 @@ class Part:
             self.sa.attn_fwd_block_sparse(self.q, self.ks[0], self.vs[0], self.bm, causal=w.causal,
                                           scale=w.scale, key_padding_mask=self.mask,
                                           alibi_slopes=self.slopes, out=self.out, lse=self.lse)
+        elif w.decode and self.fused:
+            self.sa.attn_decode_fused(self.q, self.ks[i], self.vs[i], scale=w.scale,
+                                      key_padding_mask=self.mask, alibi_slopes=self.slopes,
+                                      out=self.out, lse=self.lse, workspace=self.ws)
         elif w.decode:
             self.sa.attn_decode(self.q, self.ks[i], self.vs[i], scale=w.scale,
                                 key_padding_mask=self.mask, alibi_slopes=self.slopes,
@@ -461,7 +475,8 @@ def main():
         gbs = kv_bytes(p.w) / (t * 1e-3) / 1e9
         dec = {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": read_traffic("decode_kernel", p.w.name),
-               "kernels": "decode_kernel + decode_merge_kernel", "workload": p.w.name,
+               "kernels": "decode_kernel (single-kernel mode)" if p.fused else "decode_kernel + decode_merge_kernel",
+               "workload": p.w.name + (" single-kernel" if p.fused else ""),
                "avg_call_us": round(t * 1e3, 2), "kv_bytes_per_call": kv_bytes(p.w)}
         if prefill:
             result["decode"] = dec

@@ -14,6 +14,8 @@ Functions keep the names of the C entry points:
 * ``attn_decode(q, k_cache, v_cache, scale=None, key_padding_mask=None,
   alibi_slopes=None, out=None, lse=None, workspace=None, return_lse=True)``
 * ``decode_workspace_size(B, H_q, S_k, D)`` and ``decode_num_splits(...)``
+* ``attn_decode_fused(...)`` (one cooperative kernel) and
+  ``decode_fused_workspace(B, H_q, S_k, D, device)``
 * ``attn_fwd_block_sparse(q, k, v, block_mask, causal=False, ...)``
 * ``attn_fwd_ext(q, k, v, causal=False, ..., attn_bias=None, dropout_p=0.0,
   seed=0, offset=0)``
@@ -48,6 +50,8 @@ SIGNATURES = {
     "sa_attn_decode_workspace_size": (_SZ, [_I, _I, _I, _I]),
     "sa_attn_decode": (_I, [_VP, _VP, _VP, _VP, _FP, _I, _I, _I, _I, _I, _F, _U8P, _FP, _I, _VP, _SZ, _VP]),
     "sa_attn_decode_num_splits": (_I, [_I, _I, _I, _I, _I]),
+    "sa_attn_decode_fused_workspace_size": (_SZ, [_I, _I, _I, _I]),
+    "sa_attn_decode_fused": (_I, [_VP, _VP, _VP, _VP, _FP, _I, _I, _I, _I, _I, _F, _U8P, _FP, _I, _VP, _SZ, _VP]),
     "sa_attn_bwd_workspace_size": (_SZ, [_I, _I, _I]),
     "sa_attn_bwd": (_I, [_VP, _VP, _VP, _VP, _VP, _FP, _VP, _VP, _VP, _I, _I, _I, _I, _I, _I, _F,
                          _I, _U8P, _FP, _I, _VP, _SZ, _VP]),
@@ -267,16 +271,8 @@ def decode_workspace(B: int, H_q: int, S_k: int, D: int, device) -> torch.Tensor
     return torch.empty(max(n, 16), dtype=torch.uint8, device=device)
 
 
-def attn_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
-                scale: Optional[float] = None, key_padding_mask: Optional[torch.Tensor] = None,
-                alibi_slopes: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
-                lse: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
-                return_lse: bool = True):
-    """Single-token attention through ``sa_attn_decode`` (split-KV + merge).
-
-    q ``[B, 1, H_q, D]``; k_cache/v_cache ``[B, S_k, H_kv, D]``.  Returns
-    ``out [B, 1, H_q, D]`` (and float32 ``lse [B, H_q, 1]``).
-    """
+def _decode_prepare(q, k_cache, v_cache, key_padding_mask, alibi_slopes, out, lse, return_lse, scale):
+    """Checks and output allocation shared by the two decodes."""
     _need(q, "q")
     if q.dtype not in _DTYPE:
         raise ValueError(f"unsupported dtype {q.dtype}")
@@ -299,14 +295,58 @@ def attn_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
         lse = torch.empty((B, H_q, 1), dtype=torch.float32, device=dev)
     if lse is not None:
         _need(lse, "lse", torch.float32, (B, H_q, 1), dev)
+    sc = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    return dev, (B, S_k, H_q, H_kv, D), mask, out, lse, sc
+
+
+def attn_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                scale: Optional[float] = None, key_padding_mask: Optional[torch.Tensor] = None,
+                alibi_slopes: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
+                lse: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+                return_lse: bool = True):
+    """Single-token attention through ``sa_attn_decode`` (split-KV + merge).
+
+    q ``[B, 1, H_q, D]``; k_cache/v_cache ``[B, S_k, H_kv, D]``.  Returns
+    ``out [B, 1, H_q, D]`` (and float32 ``lse [B, H_q, 1]``).
+    """
+    dev, (B, S_k, H_q, H_kv, D), mask, out, lse, sc = _decode_prepare(
+        q, k_cache, v_cache, key_padding_mask, alibi_slopes, out, lse, return_lse, scale)
     if workspace is None:
         workspace = decode_workspace(B, H_q, S_k, D, dev)
     _need(workspace, "workspace", None, None, dev)
-    sc = 1.0 / math.sqrt(D) if scale is None else float(scale)
     st = lib().sa_attn_decode(q.data_ptr(), _ptr(k_cache), _ptr(v_cache), out.data_ptr(), _ptr(lse),
                               B, S_k, H_q, H_kv, D, sc, _ptr(mask), _ptr(alibi_slopes),
                               _DTYPE[q.dtype], workspace.data_ptr(),
                               workspace.numel() * workspace.element_size(), _stream(dev))
+    _check(st)
+    return (out, lse) if return_lse else out
+
+
+def decode_fused_workspace(B: int, H_q: int, S_k: int, D: int, device) -> torch.Tensor:
+    """A zeroed device byte buffer for ``attn_decode_fused`` at these sizes
+    (its barrier state must start at zero; calls leave it ready for reuse)."""
+    n = int(lib().sa_attn_decode_fused_workspace_size(B, H_q, S_k, D))
+    return torch.zeros(max(n, 2048), dtype=torch.uint8, device=device)
+
+
+def attn_decode_fused(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                      scale: Optional[float] = None, key_padding_mask: Optional[torch.Tensor] = None,
+                      alibi_slopes: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
+                      lse: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+                      return_lse: bool = True):
+    """Single-token attention through ``sa_attn_decode_fused`` (one cooperative
+    kernel: splits, grid barrier, merge).  As ``attn_decode``; a ``workspace``
+    passed in must come from ``decode_fused_workspace`` (or be zeroed the same
+    way) and be reused only by calls ordered on one stream."""
+    dev, (B, S_k, H_q, H_kv, D), mask, out, lse, sc = _decode_prepare(
+        q, k_cache, v_cache, key_padding_mask, alibi_slopes, out, lse, return_lse, scale)
+    if workspace is None:
+        workspace = decode_fused_workspace(B, H_q, S_k, D, dev)
+    _need(workspace, "workspace", None, None, dev)
+    st = lib().sa_attn_decode_fused(q.data_ptr(), _ptr(k_cache), _ptr(v_cache), out.data_ptr(), _ptr(lse),
+                                    B, S_k, H_q, H_kv, D, sc, _ptr(mask), _ptr(alibi_slopes),
+                                    _DTYPE[q.dtype], workspace.data_ptr(),
+                                    workspace.numel() * workspace.element_size(), _stream(dev))
     _check(st)
     return (out, lse) if return_lse else out
 
@@ -361,7 +401,8 @@ def attn_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torch.Tenso
     return dq, dk, dv
 
 
-__all__ = ["attn_fwd", "attn_fwd_block_sparse", "attn_fwd_ext", "SPARSE_BLOCK", "attn_decode", "attn_bwd", "bwd_workspace_size", "decode_workspace_size", "decode_num_splits",
+__all__ = ["attn_fwd", "attn_fwd_block_sparse", "attn_fwd_ext", "SPARSE_BLOCK", "attn_decode",
+           "attn_decode_fused", "decode_fused_workspace", "attn_bwd", "bwd_workspace_size", "decode_workspace_size", "decode_num_splits",
            "decode_workspace", "lib", "last_error", "status_string", "SaAttnError",
            "SIGNATURES", "LIB_PATH", "SA_OK", "SA_ERR_INVALID_ARG", "SA_ERR_UNSUPPORTED",
            "SA_ERR_WORKSPACE", "SA_ERR_HIP", "SA_F16", "SA_BF16"]

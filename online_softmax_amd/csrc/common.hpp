@@ -137,6 +137,17 @@ __device__ inline u32x4 buffer_load16(__amdgpu_buffer_rsrc_t rsrc, uint32_t voff
   return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rsrc, voffset, soffset, 0));
 }
 
+// Device-coherent (sc1) 16-byte buffer store and load: they write through and
+// read past the per-XCD L2 caches, so workgroups on different XCDs see each
+// other's data once the store has completed, without a cache-wide write-back
+// or invalidation.
+__device__ inline void buffer_store16_coherent(__amdgpu_buffer_rsrc_t rsrc, uint32_t voffset, u32x4 v) {
+  __builtin_amdgcn_raw_buffer_store_b128(v, rsrc, voffset, 0, 16);
+}
+__device__ inline u32x4 buffer_load16_coherent(__amdgpu_buffer_rsrc_t rsrc, uint32_t voffset) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rsrc, voffset, 0, 16));
+}
+
 // Wait for this wave's outstanding vector-memory operations, including
 // global-to-LDS copies (vmcnt(0); the other counters are left alone).
 __device__ inline void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0f70); }

@@ -23,6 +23,16 @@
 // global memory into a wave-private LDS slot and read transposed with
 // ds_read_b64_tr_b16.  Each wave issues every copy and load of a round of
 // NSUB sub-tiles before computing any of them.
+//
+// Single-kernel mode (for small batches, where the second launch costs as
+// much as the work: the "StreamAttention" page, "Seed-Only Serving Wedge",
+// finds merge and launch overhead dominant below batch 4 and calls for a
+// single-kernel cooperative split design): the same workgroups, launched
+// cooperatively so that all are resident, hand their partials over with
+// device-coherent stores, meet at a grid barrier (an arrival counter and a
+// generation word in the workspace, device-scope atomics, a bounded spin),
+// and then merge the (batch, query head, 16-wide slice of D) items between
+// them exactly as the merge kernel does.
 #pragma once
 #include "common.hpp"
 #include "host_logic.hpp"
@@ -46,7 +56,55 @@ struct DecArgs {
   int B, S_k, H_q, H_kv, G, n_hg, splits, chunk;
   float scale2;       // scale * log2(e)
   float alibi2;       // 1 / |scale|: bias to accumulator units
+  // Single-kernel mode: barrier words (see decode_grid_barrier) and the most
+  // polls a waiting workgroup makes before it gives up.
+  unsigned* bar;
+  int spin_limit;
 };
+
+// Grid barrier of the single-kernel mode, in two levels so that no counter
+// takes more than a few dozen of the device-scope atomic adds (on one address
+// they serialise): workgroup i arrives on sub-counter i % 8, the last to
+// arrive there on the root counter, and the last root arrival resets the root
+// and advances the generation word that the others poll.  Every workgroup's
+// partial stores have completed (vmcnt 0) before its arrival.  The poll is
+// bounded: a workgroup that waits spin_limit polls records a timeout and goes
+// on, so no wave can wait forever.  Words (32-bit, one 128-byte line each):
+// sub-counters 0..7 at line 0..7, root at line 8, generation at line 9,
+// timeout flag at line 10.
+constexpr int kBarLine = 32;  // 32-bit words per 128-byte line
+__device__ inline void decode_grid_barrier(unsigned* bar, unsigned nwg, int spin_limit) {
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    __builtin_amdgcn_s_waitcnt(0);
+    unsigned* gen_w = bar + 9 * kBarLine;
+    const unsigned gen = __hip_atomic_load(gen_w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const unsigned slot = blockIdx.x % 8u;
+    const unsigned n_slot = (nwg - slot + 7u) / 8u;          // workgroups with this residue
+    const unsigned n_root = nwg < 8u ? nwg : 8u;             // non-empty sub-counters
+    bool last = false;
+    if (__hip_atomic_fetch_add(bar + slot * kBarLine, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+        n_slot - 1u) {
+      __hip_atomic_store(bar + slot * kBarLine, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      last = __hip_atomic_fetch_add(bar + 8 * kBarLine, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+             n_root - 1u;
+    }
+    if (last) {
+      __hip_atomic_store(bar + 8 * kBarLine, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(gen_w, gen + 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    } else {
+      int polls = 0;
+      while (__hip_atomic_load(gen_w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == gen) {
+        __builtin_amdgcn_s_sleep(2);
+        if (++polls >= spin_limit) {
+          __hip_atomic_store(bar + 10 * kBarLine, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          break;
+        }
+      }
+    }
+  }
+  __syncthreads();
+}
 
 // Chunk swizzle of a V row in a wave's LDS slot (16-byte chunks): spreads the
 // 16 rows x 32 bytes of one transposed read over the banks.
@@ -56,7 +114,11 @@ __device__ inline int dec_swizzle(int r) {
   else return 2 * ((r >> 1) & 3);
 }
 
-template <class T, int D, bool MASK, bool ALIBI>
+template <class T, int D, bool COH>
+__device__ void merge_one(const float* ws_o, const float* ws_lse, uint16_t* out, float* lse, int splits,
+                          int item, float* s_w, float (*s_red)[4], f32x4 (*s_acc)[4]);
+
+template <class T, int D, bool MASK, bool ALIBI, bool COOP = false>
 __global__ __launch_bounds__(256, 2) void decode_kernel(DecArgs a) {
   constexpr int KK = D / 32;             // MFMA k-steps (32 wide) over the head dimension
   constexpr int DB = D / 16;             // 16-row blocks of O^T
@@ -284,10 +346,35 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(DecArgs a) {
     if (hvalid) {
       const size_t idx = ((size_t)b * a.H_q + h) * a.splits + s;
       const float inv = L > 0.f ? 1.f / L : 0.f;
-      float* op = a.ws_o + idx * D + 4 * g4;
+      const float lv = L > 0.f ? M + __log2f(L) : kNegInf;
+      if constexpr (COOP) {
+        // Handed to other workgroups: device-coherent stores (the partial
+        // area is below 4 GiB, checked on the host).
+        const auto ro = buffer_rsrc_t(a.ws_o, 0xFFFFFFFFu);
+        const uint32_t ob = (uint32_t)((idx * D + 4 * g4) * 4);
 #pragma unroll
-      for (int db = 0; db < DB; ++db) *(f32x4*)(op + 16 * db) = o[db] * inv;
-      if (g4 == 0) a.ws_lse[idx] = L > 0.f ? M + __log2f(L) : kNegInf;
+        for (int db = 0; db < DB; ++db)
+          buffer_store16_coherent(ro, ob + 64 * db, __builtin_bit_cast(u32x4, o[db] * inv));
+        if (g4 == 0) __hip_atomic_store(a.ws_lse + idx, lv, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      } else {
+        float* op = a.ws_o + idx * D + 4 * g4;
+#pragma unroll
+        for (int db = 0; db < DB; ++db) *(f32x4*)(op + 16 * db) = o[db] * inv;
+        if (g4 == 0) a.ws_lse[idx] = lv;
+      }
+    }
+  }
+  if constexpr (COOP) {
+    decode_grid_barrier(a.bar, gridDim.x, a.spin_limit);
+    // Merge phase: items (batch * query head, 16-wide slice of D) dealt out
+    // over the grid; the split's LDS is free again.
+    float* s_w = (float*)smem;
+    float(*s_red)[4] = (float(*)[4])(smem + 4 * kDecodeMaxSplits);
+    f32x4(*s_acc)[4] = (f32x4(*)[4])(smem + 4 * kDecodeMaxSplits + 64);
+    const int items = a.B * a.H_q * (D / 16);
+    for (int it = blockIdx.x; it < items; it += gridDim.x) {
+      merge_one<T, D, true>(a.ws_o, a.ws_lse, a.out, a.lse, a.splits, it, s_w, s_red, s_acc);
+      __syncthreads();
     }
   }
 }
@@ -300,28 +387,40 @@ struct MergeArgs {
   int splits;
 };
 
-// One workgroup per (batch * query head, 16-wide slice of D): out = sum_s w_s
-// o_s / sum_s w_s with w_s = exp2(lse_s - max lse) (splits with lse_s = -inf
-// weigh nothing); lse = (max + log2 sum w) ln 2.  Thread t loads the 4-wide
-// d chunk t % 4 of split t / 4 (+ 64 x): every load of the workgroup is
-// issued before any is used.
-template <class T, int D>
-__global__ __launch_bounds__(256) void decode_merge_kernel(MergeArgs a) {
+// One (batch * query head, 16-wide slice of D) item: out = sum_s w_s o_s /
+// sum_s w_s with w_s = exp2(lse_s - max lse) (splits with lse_s = -inf weigh
+// nothing); lse = (max + log2 sum w) ln 2.  Thread t of the 256 loads the
+// 4-wide d chunk t % 4 of split t / 4 (+ 64 x): every load of the workgroup is
+// issued before any is used.  COH: the partials come from other workgroups of
+// the same launch and are read device-coherently.
+template <class T, int D, bool COH>
+__device__ void merge_one(const float* ws_o, const float* ws_lse, uint16_t* out, float* lse, int splits,
+                          int item, float* s_w, float (*s_red)[4], f32x4 (*s_acc)[4]) {
   constexpr int NX = kDecodeMaxSplits / 64;
-  __shared__ float s_w[kDecodeMaxSplits];
-  __shared__ float s_red[4][4];
-  __shared__ f32x4 s_acc[4][4];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int bh = blockIdx.x / (D / 16), slice = blockIdx.x % (D / 16);
-  const int ns = a.splits;
-  const float* lp = a.ws_lse + (size_t)bh * ns;
-  const float* op = a.ws_o + (size_t)bh * ns * D + 16 * slice + 4 * (tid & 3);
-  const float lv = tid < ns ? lp[tid] : kNegInf;
+  const int bh = item / (D / 16), slice = item % (D / 16);
+  const int ns = splits;
+  const float* lp = ws_lse + (size_t)bh * ns;
+  const size_t obase = (size_t)bh * ns * D + 16 * slice + 4 * (tid & 3);
+  float lv;
   f32x4 ov[NX];
+  if constexpr (COH) {
+    lv = tid < ns ? __hip_atomic_load(lp + tid, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : kNegInf;
+    const auto ro = buffer_rsrc_t(ws_o, 0xFFFFFFFFu);
 #pragma unroll
-  for (int x = 0; x < NX; ++x) {
-    const int sp = (tid >> 2) + 64 * x;
-    ov[x] = sp < ns ? *(const f32x4*)(op + (size_t)sp * D) : (f32x4){};
+    for (int x = 0; x < NX; ++x) {
+      const int sp = (tid >> 2) + 64 * x;
+      ov[x] = sp < ns ? __builtin_bit_cast(f32x4, buffer_load16_coherent(ro, (uint32_t)((obase + (size_t)sp * D) * 4)))
+                      : (f32x4){};
+    }
+  } else {
+    lv = tid < ns ? lp[tid] : kNegInf;
+    const float* op = ws_o + obase;
+#pragma unroll
+    for (int x = 0; x < NX; ++x) {
+      const int sp = (tid >> 2) + 64 * x;
+      ov[x] = sp < ns ? *(const f32x4*)(op + (size_t)sp * D) : (f32x4){};
+    }
   }
   // Largest lse over the splits, then the weights and their sum.
   float m = lv;
@@ -356,10 +455,18 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(MergeArgs a) {
     const f32x4 sum = s_acc[0][tid] + s_acc[1][tid] + s_acc[2][tid] + s_acc[3][tid];
     const float inv = tot > 0.f ? 1.f / tot : 0.f;
     const uint2 pk = {T::pack2(sum[0] * inv, sum[1] * inv), T::pack2(sum[2] * inv, sum[3] * inv)};
-    *(uint2*)(a.out + (size_t)bh * D + 16 * slice + 4 * tid) = pk;
-    if (tid == 0 && slice == 0 && a.lse)
-      a.lse[bh] = tot > 0.f ? (M + __log2f(tot)) * kLn2 : kNegInf;
+    *(uint2*)(out + (size_t)bh * D + 16 * slice + 4 * tid) = pk;
+    if (tid == 0 && slice == 0 && lse) lse[bh] = tot > 0.f ? (M + __log2f(tot)) * kLn2 : kNegInf;
   }
+}
+
+// The second kernel of the two-kernel decode: one workgroup per item.
+template <class T, int D>
+__global__ __launch_bounds__(256) void decode_merge_kernel(MergeArgs a) {
+  __shared__ float s_w[kDecodeMaxSplits];
+  __shared__ float s_red[4][4];
+  __shared__ f32x4 s_acc[4][4];
+  merge_one<T, D, false>(a.ws_o, a.ws_lse, a.out, a.lse, a.splits, blockIdx.x, s_w, s_red, s_acc);
 }
 
 }  // namespace sa

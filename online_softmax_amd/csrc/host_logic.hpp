@@ -38,6 +38,11 @@ constexpr int kDecodeHeadGroup = 16;
 // 32 keys); the last round of a split may run past its end.
 constexpr int kDecodeRoundKeys = 512;
 
+// Single-kernel decode: bytes of barrier state at the start of its workspace
+// (eight sub-counters, a root counter, the generation word and the timeout
+// flag, one 128-byte line each), zero before the first call.
+constexpr int kDecodeBarrierBytes = 2048;
+
 // Block-sparse prefill: block size for query rows and keys (the default
 // attention block of the "Stem" page, section 6), and the capacity of a
 // workgroup's list of 64-key tiles, which bounds S_k at 64 * kSparseMaxTiles.
@@ -55,6 +60,10 @@ const char* status_string(int status);
 // when the call is valid but has nothing to compute.
 int check_fwd(const FwdShape& s, bool* noop);
 int check_decode(const DecodeShape& s, bool* noop);
+// The single-kernel decode: check_decode on the partial area after the
+// barrier state, plus the barrier area itself.
+int check_decode_fused(const DecodeShape& s, bool* noop);
+size_t decode_fused_workspace_size(int B, int H_q, int S_k, int D);
 int check_bwd(const BwdShape& s, bool* noop);
 // Additive bias and dropout of the extended forward.
 struct ExtShape {

@@ -120,3 +120,86 @@ def test_decode_deterministic():
     inp = make_inputs(Workload("dec_det", 2, 1, 3000, 14, 2, 64, "fp16", random_tail=100, seed=50))
     a, b = run_decode(inp), run_decode(inp)
     assert (a[0] == b[0]).all() and (a[1] == b[1]).all()
+
+
+# ---------------------------------------------------------------- single kernel
+
+FUSED_CASES = [
+    Workload("fu_b1_32k", 1, 1, 32768, 14, 2, 64, "fp16", decode=True, seed=56),
+    Workload("fu_b2_32k_mask", 2, 1, 32768, 14, 2, 64, "fp16", decode=True, random_tail=900, seed=57),
+    Workload("fu_b3_alibi_d128", 3, 1, 5000, 8, 2, 128, "bf16", decode=True, alibi=True, seed=58),
+    Workload("fu_b1_g40", 1, 1, 3000, 40, 1, 64, "fp16", decode=True, seed=59),
+    Workload("fu_b2_short_all", 2, 1, 129, 28, 4, 128, "bf16", decode=True, alibi=True, random_tail=60, seed=60),
+    Workload("fu_b1_k1", 1, 1, 1, 4, 4, 64, "fp16", decode=True, seed=61),
+]
+
+
+def barrier_words(ws):
+    """(sum of the arrival counters, timed out) of the single-kernel decode's
+    barrier state (32-bit words, one 128-byte line each: eight sub-counters,
+    the root counter, the generation, the timeout flag)."""
+    w = ws[:2048].cpu().view(torch.int32)[::32].tolist()
+    return sum(w[:9]), w[10]
+
+
+def run_fused(inp, ws=None):
+    q, k, v, m, s = to_dev(inp)
+    out, lse = sa.attn_decode_fused(q, k, v, scale=inp.w.scale, key_padding_mask=m, alibi_slopes=s,
+                                    workspace=ws)
+    torch.cuda.synchronize()
+    return to_f64(out.cpu()), lse.cpu().double().numpy()
+
+
+@pytest.mark.parametrize("w", FUSED_CASES, ids=lambda w: w.name)
+def test_decode_fused_cases(w):
+    inp = make_inputs(w)
+    print(f"[decode fused] {w.name} B={w.B} S_k={w.S_k} H={w.H_q}/{w.H_kv} D={w.D} {w.dtype}", flush=True)
+    ws = sa.decode_fused_workspace(w.B, w.H_q, w.S_k, w.D, "cuda")
+    out, lse = run_fused(inp, ws)
+    assert barrier_words(ws) == (0, 0)
+    ref_o, ref_l = oracle_for(inp, causal=False)
+    dt = torch.float16 if w.dtype == "fp16" else torch.bfloat16
+    assert_out_close(out, ref_o, dt, w.name)
+    assert_lse_close(lse, ref_l, w.name)
+    # The two-kernel decode agrees (the split counts may differ).
+    o2, l2 = run_decode(inp)
+    assert np.abs(out - o2).max() <= 2e-3 and np.nanmax(np.abs(np.where(np.isinf(l2), 0, lse - l2))) <= 1e-4
+
+
+def test_decode_fused_config4():
+    inp = make_inputs(WORKLOADS["c4_decode_32k"])
+    print("[decode fused] c4_decode_32k", flush=True)
+    out, lse = run_fused(inp)
+    ref_o, ref_l = oracle_for(inp, causal=False)
+    assert_out_close(out, ref_o, torch.float16, "c4 fused")
+    assert_lse_close(lse, ref_l, "c4 fused")
+
+
+def test_decode_fused_workspace_reuse():
+    """One zeroed workspace serves calls of different shapes in a row; the
+    barrier state is back at zero arrivals and no timeout after each."""
+    ws = sa.decode_fused_workspace(3, 40, 40000, 128, "cuda")
+    for i, w in enumerate([FUSED_CASES[0], FUSED_CASES[2], FUSED_CASES[3], FUSED_CASES[0], FUSED_CASES[4]]):
+        inp = make_inputs(w)
+        print(f"[decode fused reuse] call {i}: {w.name}", flush=True)
+        out, lse = run_fused(inp, ws)
+        assert barrier_words(ws) == (0, 0)
+        ref_o, ref_l = oracle_for(inp, causal=False)
+        dt = torch.float16 if w.dtype == "fp16" else torch.bfloat16
+        assert_out_close(out, ref_o, dt, w.name)
+        assert_lse_close(lse, ref_l, w.name)
+
+
+def test_decode_fused_deterministic():
+    inp = make_inputs(FUSED_CASES[1])
+    a, b = run_fused(inp), run_fused(inp)
+    assert (a[0] == b[0]).all() and (a[1] == b[1]).all()
+
+
+def test_decode_fused_workspace_errors():
+    w = FUSED_CASES[0]
+    q, k, v, _, _ = to_dev(make_inputs(w))
+    small = torch.zeros(128, dtype=torch.uint8, device="cuda")
+    with pytest.raises(sa.SaAttnError) as e:
+        sa.attn_decode_fused(q, k, v, workspace=small)
+    assert e.value.status == sa.SA_ERR_WORKSPACE

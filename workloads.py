@@ -68,6 +68,11 @@ WORKLOADS = {
     "c4_decode_32k": Workload("c4_decode_32k", 4, 1, 32768, 14, 2, 64, "fp16",
                               seed=4, decode=True,
                               note="GQA 7:1 decode, all 32768 keys valid"),
+    # The same decode at the small batches the single-kernel decode is for.
+    "decode_32k_b1": Workload("decode_32k_b1", 1, 1, 32768, 14, 2, 64, "fp16", seed=4, decode=True,
+                              note="c4_decode_32k at batch 1"),
+    "decode_32k_b2": Workload("decode_32k_b2", 2, 1, 32768, 14, 2, 64, "fp16", seed=4, decode=True,
+                              note="c4_decode_32k at batch 2"),
     "c5_alibi_8192": Workload("c5_alibi_8192", 2, 8192, 8192, 32, 32, 128, "bf16",
                               causal=True, random_tail=512, alibi=True, seed=5,
                               note="causal + ALiBi + random padding tail"),
