@@ -215,6 +215,15 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
           dp[jb] = T::mma(*(const u32x4*)&vt[off16], doreg[kk], dp[jb]);
         }
       const bool masked = n0 + BN > a.S_k || (CAUSAL && n0 + BN - 1 > wrow0 + off) || MASK;
+      // Padding bits of the tile's 64 keys (the same for every row): lane l
+      // reads the byte of key n0 + l, one ballot gathers them (bit l kept),
+      // shifted to this lane's half (keys from 4 g on).
+      uint64_t keep = ~uint64_t(0);
+      if (MASK) {
+        const int kl = n0 + lane;
+        const bool kept = kl < a.S_k && mrow[kl < a.S_k ? kl : 0] != 0;
+        keep = __builtin_amdgcn_ballot_w64(kept) >> (4 * g);
+      }
       uint32_t pk[2][8];
 #pragma unroll
       for (int jb = 0; jb < 2; ++jb)
@@ -225,10 +234,11 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
           for (int e = 0; e < 2; ++e) {
             float sv = s[jb][r + e];
             if (masked) {
-              const int kj = n0 + 4 * g + 32 * jb + 8 * ((r + e) >> 2) + ((r + e) & 3);
+              const int ko = 32 * jb + 8 * ((r + e) >> 2) + ((r + e) & 3);  // from n0 + 4 g
+              const int kj = n0 + 4 * g + ko;
               bool vis = kj < a.S_k;
               if (CAUSAL) vis = vis && kj <= ipos;
-              if (MASK) vis = vis && mrow[vis ? kj : 0] != 0;
+              if (MASK) vis = vis && ((keep >> ko) & 1u);
               sv = vis ? sv : kNegInf;
             }
             const float p = fast_exp2(fmaf(sv, sc2, -l2));

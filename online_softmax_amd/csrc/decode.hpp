@@ -250,13 +250,22 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(DecArgs a) {
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) sc[kb] = T::mma16(kr[v][kb][kk], qreg[kk], sc[kb]);
       if (MASK || kbase + 32 > k1) {
+        // Padding bits of the sub-tile's 32 keys: lane l (and l + 32) reads
+        // the byte of key kbase + l % 32, one ballot gathers them, shifted to
+        // this lane's quarter (keys from 4 g4 on).
+        uint64_t keep = ~uint64_t(0);
+        if (MASK) {
+          const int kl = kbase + (lane & 31);
+          const bool kept = kl < k1 && mrow[kl < k1 ? kl : 0] != 0;
+          keep = __builtin_amdgcn_ballot_w64(kept) >> (4 * g4);
+        }
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
             const int kj = kbase + 16 * kb + 4 * g4 + r;
             bool vis = kj < k1;
-            if (MASK) vis = vis && mrow[vis ? kj : 0] != 0;
+            if (MASK) vis = vis && ((keep >> (16 * kb + r)) & 1u);
             sc[kb][r] = vis ? sc[kb][r] : kNegInf;
           }
       }

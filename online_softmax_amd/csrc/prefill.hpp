@@ -268,19 +268,23 @@ __global__ __launch_bounds__(NW * 64, EXT ? 1 : 2) void fwd_kernel(FwdArgs a) {
   }
 
   // One bit per tile: every key of the tile is kept by the padding mask.
-  // Each wave checks 16 tiles per round, four lanes of 16 keys per tile.
+  // Each wave checks 16 tiles per round, four lanes of 16 keys per tile.  The
+  // mask row is read through a buffer resource that ends at S_k (keys past
+  // it read 0, i.e. not kept), so all sixteen loads of a lane are in flight
+  // together (a short-circuit test would wait for each in turn).
   if (MASK) {
     for (int x = tid; x < kMaskFlagTiles / 32; x += NW * 64) Mf[x] = 0;
     __syncthreads();
     const int ntf = min(ntd, kMaskFlagTiles);
+    const auto mr = buffer_rsrc_t(mrow, (uint32_t)a.S_k);
     for (int t0 = 16 * w; t0 < ntf; t0 += 16 * NW) {
       const int j0 = (t0 + (lane >> 2)) * BN + 16 * (lane & 3);
+      uint32_t kept[16];
+#pragma unroll
+      for (int e = 0; e < 16; ++e) kept[e] = __builtin_amdgcn_raw_buffer_load_b8(mr, (uint32_t)(j0 + e), 0, 0);
       bool keep = true;
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int j = j0 + e;
-        keep = keep && j < a.S_k && mrow[j < a.S_k ? j : 0] != 0;
-      }
+      for (int e = 0; e < 16; ++e) keep = keep & (kept[e] != 0);
       const uint64_t bal = __builtin_amdgcn_ballot_w64(keep);
       const bool tile_ok = lane < 16 && ((bal >> (4 * lane)) & 0xfull) == 0xfull && t0 + lane < ntf;
       const uint64_t bits = __builtin_amdgcn_ballot_w64(tile_ok);
@@ -363,14 +367,33 @@ __global__ __launch_bounds__(NW * 64, EXT ? 1 : 2) void fwd_kernel(FwdArgs a) {
     const int t = tile_of(it);
     const int n0 = t * BN;
     const bool pad_free = !MASK || (t < kMaskFlagTiles && ((Mf[t >> 5] >> (t & 31)) & 1u));
+    // The padding bits of the tile's 64 keys are the same for every row:
+    // lane l reads the byte of key n0 + l and one ballot gathers them
+    // (bit l kept).  A lane's 32 scores need the bits of key offsets
+    // 4 g + 32 jb + 8 (r/4) + r%4: nibbles 0, 2, 4, 6 of each 32-bit half of
+    // the ballot shifted by 4 g, packed into one word (bit 16 jb + r).
+    uint32_t vis32 = ~0u;
+    if (MASK && !pad_free) {
+      const int kl = n0 + lane;
+      const bool kept = kl < a.S_k && mrow[kl < a.S_k ? kl : 0] != 0;
+      const uint64_t keep = __builtin_amdgcn_ballot_w64(kept) >> (4 * g);
+      auto pick = [](uint32_t x) {
+        x &= 0x0F0F0F0Fu;
+        x = (x | (x >> 4)) & 0x00FF00FFu;
+        return (x | (x >> 8)) & 0x0000FFFFu;
+      };
+      vis32 = pick((uint32_t)keep) | (pick((uint32_t)(keep >> 32)) << 16);
+    }
 #pragma unroll
     for (int jb = 0; jb < 2; ++jb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
+        // Bitwise tests (no short-circuit), so that the pass is straight-line
+        // selects rather than a branch per score.
         const int kj = n0 + 4 * g + 32 * jb + 8 * (r >> 2) + (r & 3);
         bool vis = kj < a.S_k;
-        if (CAUSAL) vis = vis && kj <= ipos;
-        if (MASK && !pad_free) vis = vis && mrow[vis ? kj : 0] != 0;
+        if (CAUSAL) vis = vis & (kj <= ipos);
+        if (MASK) vis = vis & (((vis32 >> (16 * jb + r)) & 1u) != 0);
         s[jb][r] = vis ? s[jb][r] : kNegInf;
       }
   };
@@ -661,6 +684,14 @@ __global__ __launch_bounds__(NW * 64, EXT ? 1 : 2) void fwd_kernel(FwdArgs a) {
   // pattern of interleave_schedule, which measured faster there.
   // `keep` holds the dropout bits of tile t (all ones without dropout).
   auto full_step = [&](const int t, f32x16 (&s)[2], f32x16 (&sn)[2], const uint32_t keep) {
+    // With the padding mask, whether the next tile needs the masking pass
+    // reads a bit from LDS: read it here, before this step's fragment reads
+    // are issued, so that waiting for it does not wait for them too.
+    int masked_next = 0;
+    if constexpr (MASK) {
+      masked_next = __builtin_amdgcn_readfirstlane(tile_masked(t + 1) ? 1 : 0);
+      __asm__ volatile("" : "+s"(masked_next));
+    }
     const int n = copies(t);
     uint32_t pk[2][8];
     float tmax;
@@ -689,7 +720,7 @@ __global__ __launch_bounds__(NW * 64, EXT ? 1 : 2) void fwd_kernel(FwdArgs a) {
       bias_add(sn, bvn);
       remax = true;
     }
-    if (tile_masked(t + 1)) {
+    if (MASK ? masked_next != 0 : tile_masked(t + 1)) {
       mask_tile(t + 1, sn);
       remax = true;
     }
