@@ -37,8 +37,8 @@
 //    accumulator, so scores with and without bias share one softmax path;
 //  * tiles that no rule hides any key of (the bulk of the sweep) skip the
 //    masking pass; tiles on the causal diagonal, at the ragged end of the
-//    keys or with padded keys take it.  Which tiles are free of padding is
-//    worked out once per workgroup into a bit per tile;
+//    keys or from the first padded key on take it.  The first padded key is
+//    found once per workgroup;
 //  * block-sparse mode (the execution step of the "Stem: Rethinking Causal
 //    Information Flow in Sparse Attention" page, section 2.3): a workgroup
 //    of 4 waves owns one block of 128 query rows and sweeps only the key
@@ -63,9 +63,6 @@
 namespace sa {
 
 constexpr float kRescaleSlack = 8.0f;
-// Tiles whose padding bits a workgroup records (beyond this every tile takes
-// the masking pass, which stays correct).
-constexpr int kMaskFlagTiles = 4096;
 
 struct FwdArgs {
   const uint16_t* q;
@@ -141,7 +138,7 @@ __global__ __launch_bounds__(NW * 64, EXT ? 1 : 2) void fwd_kernel(FwdArgs a) {
 
   __shared__ __attribute__((aligned(1024))) uint16_t Ks[NS][BN * D];
   __shared__ __attribute__((aligned(1024))) uint16_t Vs[NS][BN * D];
-  __shared__ uint32_t Mf[MASK ? kMaskFlagTiles / 32 : 1];
+  __shared__ int Pw[MASK ? NW : 1];  // per-wave first cleared key
   __shared__ int16_t Tl[SPARSE ? kSparseMaxTiles : 1];  // block-sparse tile list
   __shared__ int Tn;                                     // its length
 
@@ -267,29 +264,33 @@ __global__ __launch_bounds__(NW * 64, EXT ? 1 : 2) void fwd_kernel(FwdArgs a) {
     }
   }
 
-  // One bit per tile: every key of the tile is kept by the padding mask.
-  // Each wave checks 16 tiles per round, four lanes of 16 keys per tile.  The
-  // mask row is read through a buffer resource that ends at S_k (keys past
-  // it read 0, i.e. not kept), so all sixteen loads of a lane are in flight
-  // together (a short-circuit test would wait for each in turn).
+  // The first key the padding mask clears among the keys this workgroup may
+  // read (S_k if none): tiles that end at or before it need no padding test,
+  // the others take the masking pass (for the usual padding, a cleared tail,
+  // that is exactly the tiles holding cleared keys).  Each lane checks 16
+  // consecutive keys per round through a buffer resource that ends at S_k
+  // (keys past it read 0 and only push the minimum to S_k or beyond), all 16
+  // loads in flight together; the minimum goes over the wave by shuffles and
+  // over the waves through LDS.
+  int pad_start = a.S_k;
   if (MASK) {
-    for (int x = tid; x < kMaskFlagTiles / 32; x += NW * 64) Mf[x] = 0;
-    __syncthreads();
-    const int ntf = min(ntd, kMaskFlagTiles);
     const auto mr = buffer_rsrc_t(mrow, (uint32_t)a.S_k);
-    for (int t0 = 16 * w; t0 < ntf; t0 += 16 * NW) {
-      const int j0 = (t0 + (lane >> 2)) * BN + 16 * (lane & 3);
+    const int nkeys = ntd * BN;
+    int first = a.S_k;
+    for (int j0 = 16 * (64 * w + lane); j0 < nkeys; j0 += 16 * 64 * NW) {
       uint32_t kept[16];
 #pragma unroll
       for (int e = 0; e < 16; ++e) kept[e] = __builtin_amdgcn_raw_buffer_load_b8(mr, (uint32_t)(j0 + e), 0, 0);
-      bool keep = true;
 #pragma unroll
-      for (int e = 0; e < 16; ++e) keep = keep & (kept[e] != 0);
-      const uint64_t bal = __builtin_amdgcn_ballot_w64(keep);
-      const bool tile_ok = lane < 16 && ((bal >> (4 * lane)) & 0xfull) == 0xfull && t0 + lane < ntf;
-      const uint64_t bits = __builtin_amdgcn_ballot_w64(tile_ok);
-      if (lane == 0 && bits) atomicOr(&Mf[t0 >> 5], (uint32_t)(bits & 0xffffu) << (t0 & 31));
+      for (int e = 15; e >= 0; --e) first = kept[e] == 0 ? min(first, j0 + e) : first;
     }
+#pragma unroll
+    for (int k = 32; k > 0; k >>= 1) first = min(first, __shfl_xor(first, k));
+    if (lane == 0) Pw[w] = first;
+    __syncthreads();
+#pragma unroll
+    for (int x = 0; x < NW; ++x) pad_start = min(pad_start, Pw[x]);
+    pad_start = __builtin_amdgcn_readfirstlane(pad_start);
   }
 
   float m_ref = kNegInf;  // reference maximum, base-2 domain (raised lazily)
@@ -360,13 +361,13 @@ __global__ __launch_bounds__(NW * 64, EXT ? 1 : 2) void fwd_kernel(FwdArgs a) {
     const int t = tile_of(it);
     const int n0 = t * BN;
     bool masked = n0 + BN > a.S_k || (CAUSAL && n0 + BN - 1 > wrow0 + off);
-    if (MASK) masked = masked || !(t < kMaskFlagTiles && ((Mf[t >> 5] >> (t & 31)) & 1u));
+    if (MASK) masked = masked || n0 + BN > pad_start;
     return masked;
   };
   auto mask_tile = [&](const int it, f32x16 (&s)[2]) {
     const int t = tile_of(it);
     const int n0 = t * BN;
-    const bool pad_free = !MASK || (t < kMaskFlagTiles && ((Mf[t >> 5] >> (t & 31)) & 1u));
+    const bool pad_free = !MASK || n0 + BN <= pad_start;
     // The padding bits of the tile's 64 keys are the same for every row:
     // lane l reads the byte of key n0 + l and one ballot gathers them
     // (bit l kept).  A lane's 32 scores need the bits of key offsets
@@ -684,14 +685,6 @@ __global__ __launch_bounds__(NW * 64, EXT ? 1 : 2) void fwd_kernel(FwdArgs a) {
   // pattern of interleave_schedule, which measured faster there.
   // `keep` holds the dropout bits of tile t (all ones without dropout).
   auto full_step = [&](const int t, f32x16 (&s)[2], f32x16 (&sn)[2], const uint32_t keep) {
-    // With the padding mask, whether the next tile needs the masking pass
-    // reads a bit from LDS: read it here, before this step's fragment reads
-    // are issued, so that waiting for it does not wait for them too.
-    int masked_next = 0;
-    if constexpr (MASK) {
-      masked_next = __builtin_amdgcn_readfirstlane(tile_masked(t + 1) ? 1 : 0);
-      __asm__ volatile("" : "+s"(masked_next));
-    }
     const int n = copies(t);
     uint32_t pk[2][8];
     float tmax;
@@ -720,7 +713,7 @@ __global__ __launch_bounds__(NW * 64, EXT ? 1 : 2) void fwd_kernel(FwdArgs a) {
       bias_add(sn, bvn);
       remax = true;
     }
-    if (MASK ? masked_next != 0 : tile_masked(t + 1)) {
+    if (tile_masked(t + 1)) {
       mask_tile(t + 1, sn);
       remax = true;
     }
