@@ -405,11 +405,20 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a) {
       } else {
         s = (f32x16){};
       }
+      // All of the tile's Q and dO fragments are read before the first MFMA
+      // (one wave per SIMD: nothing else would hide the LDS latency).
+      u32x4 qa[KK], oa[KK];
 #pragma unroll
       for (int kk = 0; kk < KK; ++kk) {
         const int off16 = li * D + 8 * ((2 * kk + g) ^ rsw);
-        s = T::mma(*(const u32x4*)&qt_[off16], kreg[kk], s);
-        dp = T::mma(*(const u32x4*)&ot_[off16], vreg[kk], dp);
+        qa[kk] = *(const u32x4*)&qt_[off16];
+        oa[kk] = *(const u32x4*)&ot_[off16];
+      }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk) {
+        s = T::mma(qa[kk], kreg[kk], s);
+        dp = T::mma(oa[kk], vreg[kk], dp);
       }
       // Rows' lse2 and Di: registers r = 4 c .. 4 c + 3 hold rows 8 c + 4 g + 0..3.
       uint32_t pk[8], dk_[8];
@@ -439,19 +448,27 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a) {
         dk_[2 * c] = T::pack2(ds[0], ds[1]);
         dk_[2 * c + 1] = T::pack2(ds[2], ds[3]);
       }
-      // dV^T += dO^T P and dK^T += Q^T dS over two 16-row steps.
+      // dV^T += dO^T P and dK^T += Q^T dS over two 16-row steps, each step's
+      // transposed fragments read before its MFMAs.
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
         const u32x4 bp = {pk[4 * ks], pk[4 * ks + 1], pk[4 * ks + 2], pk[4 * ks + 3]};
         const u32x4 bd = {dk_[4 * ks], dk_[4 * ks + 1], dk_[4 * ks + 2], dk_[4 * ks + 3]};
+        u32x4 ov[DB], qv[DB];
 #pragma unroll
         for (int db = 0; db < DB; ++db) {
           const u32x2 olo = lds_read_tr(ot_ + 16 * ks * D + tofs[0][db]);
           const u32x2 ohi = lds_read_tr(ot_ + 16 * ks * D + tofs[1][db]);
-          dv[db] = T::mma((u32x4){olo[0], olo[1], ohi[0], ohi[1]}, bp, dv[db]);
           const u32x2 qlo = lds_read_tr(qt_ + 16 * ks * D + tofs[0][db]);
           const u32x2 qhi = lds_read_tr(qt_ + 16 * ks * D + tofs[1][db]);
-          dk[db] = T::mma((u32x4){qlo[0], qlo[1], qhi[0], qhi[1]}, bd, dk[db]);
+          ov[db] = (u32x4){olo[0], olo[1], ohi[0], ohi[1]};
+          qv[db] = (u32x4){qlo[0], qlo[1], qhi[0], qhi[1]};
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+          dv[db] = T::mma(ov[db], bp, dv[db]);
+          dk[db] = T::mma(qv[db], bd, dk[db]);
         }
       }
     }
