@@ -64,7 +64,7 @@ DECODE_ROTATION_BYTES = 768 << 20
 PROFILES = ROOT / "profiles"
 # Sources each kernel is built from: a traffic figure measured on other sources is stale.
 KERNEL_SOURCES = {
-    "fwd_kernel": ["common.hpp", "prefill.hpp", "sa_attn.hip"],
+    "fwd_kernel": ["common.hpp", "host_logic.hpp", "prefill.hpp", "sa_attn.hip"],
     "decode_kernel": ["common.hpp", "host_logic.hpp", "decode.hpp", "sa_attn.hip"],
     "bwd_kernels": ["common.hpp", "host_logic.hpp", "backward.hpp", "sa_attn_bwd.hip"],
 }
