@@ -187,37 +187,36 @@ int sa_attn_decode(const void* q, const void* k_cache, const void* v_cache,
                    int dtype, void* workspace, size_t workspace_bytes, sa_stream_t stream);
 
 /*
- * Bytes of device workspace sa_attn_decode_fused needs: 2048 bytes of barrier
- * state followed by sa_attn_decode's partial area.  Pure host arithmetic;
- * returns 0 when a size is negative or the result would overflow.
+ * Bytes of device workspace sa_attn_decode_fused needs: 65536 bytes of
+ * arrival counters followed by sa_attn_decode's partial area.  Pure host
+ * arithmetic; returns 0 when a size is negative or the result would overflow.
  */
 size_t sa_attn_decode_fused_workspace_size(int B, int H_q, int S_k, int D);
 
 /*
- * sa_attn_decode as a single kernel, for small batches (the "StreamAttention"
- * page, "Seed-Only Serving Wedge": below batch 4 the second launch of a
- * split-then-merge decode costs as much as the work, and a single-kernel
- * cooperative split design is what it calls for).  The splits are launched
- * cooperatively (all resident at once), hand their partial states over
- * through the workspace, meet at a grid barrier, and merge them with
- * log-sum-exp weights in the same launch.  Same arguments, layouts, rules
- * and result as sa_attn_decode, except the workspace:
+ * sa_attn_decode as a single kernel (the "StreamAttention" page, "Seed-Only
+ * Serving Wedge": at small batch the second launch of a split-then-merge
+ * decode costs as much as the work, and a single-kernel split design is what
+ * it calls for).  The splits are the same as sa_attn_decode's; each hands its
+ * partial state over through the workspace and counts itself on its head
+ * group's arrival counter (a device-scope atomic add), and the last split of
+ * a group to arrive merges the group's partial states with log-sum-exp
+ * weights in the same launch.  No workgroup waits for another.  Same
+ * arguments, layouts, rules and result as sa_attn_decode, except the
+ * workspace:
  *
  *   workspace  at least sa_attn_decode_fused_workspace_size(B, H_q, S_k, D)
- *              bytes, 256-byte aligned.  Its first 2048 bytes hold the
- *              barrier's state: they must be zero before the first call
- *              that uses this workspace, and every call leaves them ready
- *              for the next one.  Calls sharing a workspace must be ordered
- *              (one stream); calls that may overlap need separate ones.
+ *              bytes, 256-byte aligned.  Its first 65536 bytes hold the
+ *              arrival counters (32-bit, one per head group): they must be
+ *              zero before the first call that uses this workspace, and
+ *              every call that completes leaves them zero again, so calls of
+ *              any shape can reuse it.  Calls sharing a workspace must be
+ *              ordered (one stream); calls that may overlap need separate
+ *              ones.
  *
- * The number of splits is capped so that every workgroup is resident; when
- * B * H_kv * ceil(H_q / H_kv / 16) head groups alone exceed that, the call
- * fails with SA_ERR_UNSUPPORTED (use sa_attn_decode).  The barrier's wait
- * is bounded: should a workgroup wait about a million polls (over a second),
- * it sets the word at byte 1280 of the workspace to 1 and goes on, and that
- * call's output is not valid (zero the barrier state before reusing the
- * workspace).  Errors: SA_ERR_INVALID_ARG, SA_ERR_UNSUPPORTED (also when the
- * device has no cooperative launch), SA_ERR_WORKSPACE, SA_ERR_HIP.
+ * Errors: SA_ERR_INVALID_ARG, SA_ERR_UNSUPPORTED (more than 16384 head groups
+ * B * H_kv * ceil(H_q / H_kv / 16), or partial outputs of 4 GiB or more: use
+ * sa_attn_decode), SA_ERR_WORKSPACE, SA_ERR_HIP.
  */
 int sa_attn_decode_fused(const void* q, const void* k_cache, const void* v_cache, void* out,
                          float* lse, int B, int S_k, int H_q, int H_kv, int D, float scale,

@@ -14,7 +14,7 @@ Functions keep the names of the C entry points:
 * ``attn_decode(q, k_cache, v_cache, scale=None, key_padding_mask=None,
   alibi_slopes=None, out=None, lse=None, workspace=None, return_lse=True)``
 * ``decode_workspace_size(B, H_q, S_k, D)`` and ``decode_num_splits(...)``
-* ``attn_decode_fused(...)`` (one cooperative kernel) and
+* ``attn_decode_fused(...)`` (one kernel) and
   ``decode_fused_workspace(B, H_q, S_k, D, device)``
 * ``attn_fwd_block_sparse(q, k, v, block_mask, causal=False, ...)``
 * ``attn_fwd_ext(q, k, v, causal=False, ..., attn_bias=None, dropout_p=0.0,
@@ -178,6 +178,7 @@ def attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = F
 
 
 SPARSE_BLOCK = 128  # query rows and keys per block of the block-sparse forward
+DECODE_ARRIVE_BYTES = 65536  # arrival counters at the start of a single-kernel decode workspace
 
 
 def attn_fwd_block_sparse(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
@@ -324,9 +325,9 @@ def attn_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
 
 def decode_fused_workspace(B: int, H_q: int, S_k: int, D: int, device) -> torch.Tensor:
     """A zeroed device byte buffer for ``attn_decode_fused`` at these sizes
-    (its barrier state must start at zero; calls leave it ready for reuse)."""
+    (its arrival counters must start at zero; calls leave them zero again)."""
     n = int(lib().sa_attn_decode_fused_workspace_size(B, H_q, S_k, D))
-    return torch.zeros(max(n, 2048), dtype=torch.uint8, device=device)
+    return torch.zeros(max(n, DECODE_ARRIVE_BYTES), dtype=torch.uint8, device=device)
 
 
 def attn_decode_fused(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
@@ -334,8 +335,9 @@ def attn_decode_fused(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Ten
                       alibi_slopes: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
                       lse: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
                       return_lse: bool = True):
-    """Single-token attention through ``sa_attn_decode_fused`` (one cooperative
-    kernel: splits, grid barrier, merge).  As ``attn_decode``; a ``workspace``
+    """Single-token attention through ``sa_attn_decode_fused`` (one kernel:
+    the last split of each head group to finish merges it).  As
+    ``attn_decode``; a ``workspace``
     passed in must come from ``decode_fused_workspace`` (or be zeroed the same
     way) and be reused only by calls ordered on one stream."""
     dev, (B, S_k, H_q, H_kv, D), mask, out, lse, sc = _decode_prepare(

@@ -24,15 +24,15 @@
 // ds_read_b64_tr_b16.  Each wave issues every copy and load of a round of
 // NSUB sub-tiles before computing any of them.
 //
-// Single-kernel mode (for small batches, where the second launch costs as
-// much as the work: the "StreamAttention" page, "Seed-Only Serving Wedge",
-// finds merge and launch overhead dominant below batch 4 and calls for a
-// single-kernel cooperative split design): the same workgroups, launched
-// cooperatively so that all are resident, hand their partials over with
-// device-coherent stores, meet at a grid barrier (an arrival counter and a
-// generation word in the workspace, device-scope atomics, a bounded spin),
-// and then merge the (batch, query head, 16-wide slice of D) items between
-// them exactly as the merge kernel does.
+// Single-kernel mode (the "StreamAttention" page, "Seed-Only Serving Wedge",
+// finds the merge and its launch dominant at small batch and calls for a
+// single-kernel split design): each workgroup hands its partial over with
+// device-coherent stores and then counts itself on its head group's arrival
+// counter (a device-scope atomic in the workspace).  The workgroup that
+// arrives last has every partial of the group available: it resets the
+// counter to zero for the next call and merges the group's splits itself.
+// No workgroup ever waits for another, so the launch is an ordinary one of
+// any size.
 #pragma once
 #include "common.hpp"
 #include "host_logic.hpp"
@@ -56,55 +56,9 @@ struct DecArgs {
   int B, S_k, H_q, H_kv, G, n_hg, splits, chunk;
   float scale2;       // scale * log2(e)
   float alibi2;       // 1 / |scale|: bias to accumulator units
-  // Single-kernel mode: barrier words (see decode_grid_barrier) and the most
-  // polls a waiting workgroup makes before it gives up.
-  unsigned* bar;
-  int spin_limit;
+  // Single-kernel mode: one arrival counter per head group (zero between calls).
+  unsigned* arrive;
 };
-
-// Grid barrier of the single-kernel mode, in two levels so that no counter
-// takes more than a few dozen of the device-scope atomic adds (on one address
-// they serialise): workgroup i arrives on sub-counter i % 8, the last to
-// arrive there on the root counter, and the last root arrival resets the root
-// and advances the generation word that the others poll.  Every workgroup's
-// partial stores have completed (vmcnt 0) before its arrival.  The poll is
-// bounded: a workgroup that waits spin_limit polls records a timeout and goes
-// on, so no wave can wait forever.  Words (32-bit, one 128-byte line each):
-// sub-counters 0..7 at line 0..7, root at line 8, generation at line 9,
-// timeout flag at line 10.
-constexpr int kBarLine = 32;  // 32-bit words per 128-byte line
-__device__ inline void decode_grid_barrier(unsigned* bar, unsigned nwg, int spin_limit) {
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    __builtin_amdgcn_s_waitcnt(0);
-    unsigned* gen_w = bar + 9 * kBarLine;
-    const unsigned gen = __hip_atomic_load(gen_w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    const unsigned slot = blockIdx.x % 8u;
-    const unsigned n_slot = (nwg - slot + 7u) / 8u;          // workgroups with this residue
-    const unsigned n_root = nwg < 8u ? nwg : 8u;             // non-empty sub-counters
-    bool last = false;
-    if (__hip_atomic_fetch_add(bar + slot * kBarLine, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
-        n_slot - 1u) {
-      __hip_atomic_store(bar + slot * kBarLine, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      last = __hip_atomic_fetch_add(bar + 8 * kBarLine, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
-             n_root - 1u;
-    }
-    if (last) {
-      __hip_atomic_store(bar + 8 * kBarLine, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      __hip_atomic_store(gen_w, gen + 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    } else {
-      int polls = 0;
-      while (__hip_atomic_load(gen_w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == gen) {
-        __builtin_amdgcn_s_sleep(2);
-        if (++polls >= spin_limit) {
-          __hip_atomic_store(bar + 10 * kBarLine, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          break;
-        }
-      }
-    }
-  }
-  __syncthreads();
-}
 
 // Chunk swizzle of a V row in a wave's LDS slot (16-byte chunks): spreads the
 // 16 rows x 32 bytes of one transposed read over the banks.
@@ -114,11 +68,10 @@ __device__ inline int dec_swizzle(int r) {
   else return 2 * ((r >> 1) & 3);
 }
 
-template <class T, int D, bool COH>
-__device__ void merge_one(const float* ws_o, const float* ws_lse, uint16_t* out, float* lse, int splits,
-                          int item, float* s_w, float (*s_red)[4], f32x4 (*s_acc)[4]);
+template <class T, int D>
+__device__ void merge_group(const DecArgs& a, int b, int h0, int g_heads);
 
-template <class T, int D, bool MASK, bool ALIBI, bool COOP = false>
+template <class T, int D, bool MASK, bool ALIBI, bool FUSED = false>
 __global__ __launch_bounds__(256, 2) void decode_kernel(DecArgs a) {
   constexpr int KK = D / 32;             // MFMA k-steps (32 wide) over the head dimension
   constexpr int DB = D / 16;             // 16-row blocks of O^T
@@ -128,9 +81,7 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(DecArgs a) {
   constexpr int SLOT = 32 * D;           // 16-bit words per sub-tile slot
   constexpr int VBYTES = 4 * NSUB * SLOT * 2;
   constexpr int MBYTES = 3 * (2 + D) * 16 * 4;
-  constexpr int FBYTES = 16 * kDecodeMaxSplits * 4 + 256 * 16;
-  constexpr int SB1 = VBYTES > MBYTES ? VBYTES : MBYTES;
-  constexpr int SBYTES = SB1 > FBYTES ? SB1 : FBYTES;
+  constexpr int SBYTES = VBYTES > MBYTES ? VBYTES : MBYTES;
   __shared__ __attribute__((aligned(1024))) unsigned char smem[SBYTES];
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -356,8 +307,8 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(DecArgs a) {
       const size_t idx = ((size_t)b * a.H_q + h) * a.splits + s;
       const float inv = L > 0.f ? 1.f / L : 0.f;
       const float lv = L > 0.f ? M + __log2f(L) : kNegInf;
-      if constexpr (COOP) {
-        // Handed to other workgroups: device-coherent stores (the partial
+      if constexpr (FUSED) {
+        // Handed to another workgroup: device-coherent stores (the partial
         // area is below 4 GiB, checked on the host).
         const auto ro = buffer_rsrc_t(a.ws_o, 0xFFFFFFFFu);
         const uint32_t ob = (uint32_t)((idx * D + 4 * g4) * 4);
@@ -373,17 +324,104 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(DecArgs a) {
       }
     }
   }
-  if constexpr (COOP) {
-    decode_grid_barrier(a.bar, gridDim.x, a.spin_limit);
-    // Merge phase: items (batch * query head, 16-wide slice of D) dealt out
-    // over the grid; the split's LDS is free again.
-    float* s_w = (float*)smem;
-    float(*s_red)[4] = (float(*)[4])(smem + 4 * kDecodeMaxSplits);
-    f32x4(*s_acc)[4] = (f32x4(*)[4])(smem + 4 * kDecodeMaxSplits + 64);
-    const int items = a.B * a.H_q * (D / 16);
-    for (int it = blockIdx.x; it < items; it += gridDim.x) {
-      merge_one<T, D, true>(a.ws_o, a.ws_lse, a.out, a.lse, a.splits, it, s_w, s_red, s_acc);
-      __syncthreads();
+  if constexpr (FUSED) {
+    // Count this split on the head group's arrival counter once wave 0's
+    // partial stores have completed; the last of the group's splits to
+    // arrive resets the counter and merges them all.
+    __shared__ int s_last;
+    __syncthreads();
+    if (tid == 0) {
+      __builtin_amdgcn_s_waitcnt(0);
+      unsigned* cnt = a.arrive + grp;
+      const bool last = __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+                        (unsigned)a.splits - 1u;
+      if (last) __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      s_last = last;
+    }
+    __syncthreads();
+    if (s_last) merge_group<T, D>(a, b, h0, g_heads);
+  }
+}
+
+// Online log-sum-exp state (m, l, acc) of one (head, 4-wide d chunk) over a
+// subset of splits: l = sum 2^(lse_s - m), acc = sum 2^(lse_s - m) o_s.
+// Combining two states rescales both to the larger maximum (a state with m =
+// -inf holds nothing and is scaled by zero).
+__device__ inline float lse_scale(float m, float mn) { return m == kNegInf ? 0.f : fast_exp2(m - mn); }
+
+// The merge of one head group (query heads h0 .. h0 + g_heads - 1 of batch b)
+// by the workgroup that completed it: for each head and d, out = sum_s w_s
+// o_s / sum_s w_s with w_s = 2^(lse_s - max lse), and lse = (max + log2 sum)
+// ln 2 (a split with lse_s = -inf weighs nothing).  The group's partial rows
+// (head-major, split-minor) are contiguous in the workspace.  Each thread
+// owns one (head, d chunk) pair and the splits part, part + P, ... of it (P
+// threads per pair, adjacent lanes), reads XC of those splits at a time with
+// every load of the chunk issued before any is used, and keeps an online
+// state in registers; the P states of a pair are then combined by lane
+// exchanges.  Pairs beyond 256 / P are taken in further sweeps.
+template <class T, int D>
+__device__ void merge_group(const DecArgs& a, int b, int h0, int g_heads) {
+  constexpr int TD = D / 4, XC = 32;
+  const int tid = threadIdx.x;
+  const int ns = a.splits;
+  const int npair = g_heads * TD;
+  int P = 1;
+  while (2 * P * npair <= 256 && P < ns) P *= 2;
+  const int per = 256 / P;  // pairs per sweep
+  const size_t row0 = ((size_t)b * a.H_q + h0) * ns;
+  const auto ro = buffer_rsrc_t(a.ws_o, 0xFFFFFFFFu);
+  for (int pb = 0; pb < npair; pb += per) {
+    const int pi = pb + tid / P, part = tid % P;
+    const bool act = pi < npair;
+    const int hh = pi / TD, d4 = pi - hh * TD;
+    const size_t rbase = row0 + (size_t)(act ? hh : 0) * ns;
+    float m = kNegInf, l = 0.f;
+    f32x4 acc = {};
+    for (int x0 = 0; x0 * P < ns; x0 += XC) {
+      float lv[XC];
+      f32x4 ov[XC];
+#pragma unroll
+      for (int x = 0; x < XC; ++x) {
+        const int sp = part + P * (x0 + x);
+        const bool ok = act && sp < ns;
+        lv[x] = ok ? __hip_atomic_load(a.ws_lse + rbase + sp, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : kNegInf;
+        ov[x] = ok ? __builtin_bit_cast(f32x4, buffer_load16_coherent(
+                                                   ro, (uint32_t)(((rbase + sp) * D + 4 * d4) * 4)))
+                   : (f32x4){};
+      }
+      float cm = kNegInf;
+#pragma unroll
+      for (int x = 0; x < XC; ++x) cm = fmaxf(cm, lv[x]);
+      const float mn = fmaxf(m, cm);
+      if (mn != kNegInf) {
+        const float sc = lse_scale(m, mn);
+        l *= sc;
+        acc *= sc;
+#pragma unroll
+        for (int x = 0; x < XC; ++x) {
+          const float e = fast_exp2(lv[x] - mn);
+          l += e;
+          acc += e * ov[x];
+        }
+        m = mn;
+      }
+    }
+    for (int k = 1; k < P; k <<= 1) {
+      const float om = __shfl_xor(m, k), ol = __shfl_xor(l, k);
+      f32x4 oa;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) oa[e] = __shfl_xor(acc[e], k);
+      const float mn = fmaxf(m, om);
+      const float s1 = lse_scale(m, mn), s2 = lse_scale(om, mn);
+      l = l * s1 + ol * s2;
+      acc = acc * s1 + oa * s2;
+      m = mn;
+    }
+    if (act && part == 0) {
+      const float inv = l > 0.f ? 1.f / l : 0.f;
+      const uint2 pk = {T::pack2(acc[0] * inv, acc[1] * inv), T::pack2(acc[2] * inv, acc[3] * inv)};
+      *(uint2*)(a.out + ((size_t)b * a.H_q + h0 + hh) * D + 4 * d4) = pk;
+      if (a.lse && d4 == 0) a.lse[(size_t)b * a.H_q + h0 + hh] = l > 0.f ? (m + __log2f(l)) * kLn2 : kNegInf;
     }
   }
 }
@@ -400,9 +438,8 @@ struct MergeArgs {
 // sum_s w_s with w_s = exp2(lse_s - max lse) (splits with lse_s = -inf weigh
 // nothing); lse = (max + log2 sum w) ln 2.  Thread t of the 256 loads the
 // 4-wide d chunk t % 4 of split t / 4 (+ 64 x): every load of the workgroup is
-// issued before any is used.  COH: the partials come from other workgroups of
-// the same launch and are read device-coherently.
-template <class T, int D, bool COH>
+// issued before any is used.
+template <class T, int D>
 __device__ void merge_one(const float* ws_o, const float* ws_lse, uint16_t* out, float* lse, int splits,
                           int item, float* s_w, float (*s_red)[4], f32x4 (*s_acc)[4]) {
   constexpr int NX = kDecodeMaxSplits / 64;
@@ -411,25 +448,13 @@ __device__ void merge_one(const float* ws_o, const float* ws_lse, uint16_t* out,
   const int ns = splits;
   const float* lp = ws_lse + (size_t)bh * ns;
   const size_t obase = (size_t)bh * ns * D + 16 * slice + 4 * (tid & 3);
-  float lv;
+  const float lv = tid < ns ? lp[tid] : kNegInf;
+  const float* op = ws_o + obase;
   f32x4 ov[NX];
-  if constexpr (COH) {
-    lv = tid < ns ? __hip_atomic_load(lp + tid, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : kNegInf;
-    const auto ro = buffer_rsrc_t(ws_o, 0xFFFFFFFFu);
 #pragma unroll
-    for (int x = 0; x < NX; ++x) {
-      const int sp = (tid >> 2) + 64 * x;
-      ov[x] = sp < ns ? __builtin_bit_cast(f32x4, buffer_load16_coherent(ro, (uint32_t)((obase + (size_t)sp * D) * 4)))
-                      : (f32x4){};
-    }
-  } else {
-    lv = tid < ns ? lp[tid] : kNegInf;
-    const float* op = ws_o + obase;
-#pragma unroll
-    for (int x = 0; x < NX; ++x) {
-      const int sp = (tid >> 2) + 64 * x;
-      ov[x] = sp < ns ? *(const f32x4*)(op + (size_t)sp * D) : (f32x4){};
-    }
+  for (int x = 0; x < NX; ++x) {
+    const int sp = (tid >> 2) + 64 * x;
+    ov[x] = sp < ns ? *(const f32x4*)(op + (size_t)sp * D) : (f32x4){};
   }
   // Largest lse over the splits, then the weights and their sum.
   float m = lv;
@@ -475,7 +500,7 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(MergeArgs a) {
   __shared__ float s_w[kDecodeMaxSplits];
   __shared__ float s_red[4][4];
   __shared__ f32x4 s_acc[4][4];
-  merge_one<T, D, false>(a.ws_o, a.ws_lse, a.out, a.lse, a.splits, blockIdx.x, s_w, s_red, s_acc);
+  merge_one<T, D>(a.ws_o, a.ws_lse, a.out, a.lse, a.splits, blockIdx.x, s_w, s_red, s_acc);
 }
 
 }  // namespace sa

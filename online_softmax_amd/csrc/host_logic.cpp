@@ -215,23 +215,26 @@ size_t decode_workspace_size(int B, int H_q, int S_k, int D) {
 }
 
 size_t decode_fused_workspace_size(int B, int H_q, int S_k, int D) {
+  if (B < 0 || H_q < 0 || S_k < 0 || D < 0) return 0;
   const size_t n = decode_workspace_size(B, H_q, S_k, D);
-  return n == 0 && (B < 0 || H_q < 0 || S_k < 0 || D < 0) ? 0 : n + kDecodeBarrierBytes;
+  if (n == 0 && B > 0 && H_q > 0) return 0;  // overflow
+  return n > SIZE_MAX - kDecodeArriveBytes ? 0 : n + kDecodeArriveBytes;
 }
 
 int check_decode_fused(const DecodeShape& s, bool* noop) {
   *noop = false;
   DecodeShape t = s;
-  if (s.B != 0) {
+  const int64_t ab = kDecodeArriveBytes;
+  if (s.B > 0 && s.H_q > 0) {
     if (!s.workspace)
       return fail(SA_ERR_WORKSPACE, "workspace is NULL (%zu bytes needed)",
                   decode_fused_workspace_size(s.B, s.H_q, s.S_k, s.D));
     if (!aligned(s.workspace, 256)) return fail(SA_ERR_WORKSPACE, "workspace must be 256-byte aligned");
-    if (s.workspace_bytes < (size_t)kDecodeBarrierBytes)
+    if (s.workspace_bytes < (size_t)ab)
       return fail(SA_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed", s.workspace_bytes,
                   decode_fused_workspace_size(s.B, s.H_q, s.S_k, s.D));
-    t.workspace = (const char*)s.workspace + kDecodeBarrierBytes;
-    t.workspace_bytes = s.workspace_bytes - kDecodeBarrierBytes;
+    t.workspace = (const char*)s.workspace + ab;
+    t.workspace_bytes = s.workspace_bytes - (size_t)ab;
   }
   int st = check_decode(t, noop);
   if (st != SA_OK || *noop) return st;
@@ -240,7 +243,7 @@ int check_decode_fused(const DecodeShape& s, bool* noop) {
   const void* others[7] = {s.q, s.k, s.v, s.mask, s.slopes, s.out, s.lse};
   const size_t osz[7] = {qb, kb, kb, (size_t)s.B * s.S_k, (size_t)s.H_q * 4, qb, lb};
   for (int i = 0; i < 7; ++i)
-    if (overlap(s.workspace, kDecodeBarrierBytes, others[i], osz[i]))
+    if (overlap(s.workspace, (size_t)ab, others[i], osz[i]))
       return fail(SA_ERR_INVALID_ARG, "workspace overlaps an input or output");
   return SA_OK;
 }

@@ -38,10 +38,6 @@ constexpr int kDecodeHeadGroup = 16;
 // 32 keys); the last round of a split may run past its end.
 constexpr int kDecodeRoundKeys = 512;
 
-// Single-kernel decode: bytes of barrier state at the start of its workspace
-// (eight sub-counters, a root counter, the generation word and the timeout
-// flag, one 128-byte line each), zero before the first call.
-constexpr int kDecodeBarrierBytes = 2048;
 
 // Block-sparse prefill: block size for query rows and keys (the default
 // attention block of the "Stem" page, section 6), and the capacity of a
@@ -60,8 +56,14 @@ const char* status_string(int status);
 // when the call is valid but has nothing to compute.
 int check_fwd(const FwdShape& s, bool* noop);
 int check_decode(const DecodeShape& s, bool* noop);
-// The single-kernel decode: check_decode on the partial area after the
-// barrier state, plus the barrier area itself.
+// The single-kernel decode: its workspace starts with kDecodeArriveBytes of
+// 32-bit arrival counters, one per head group (so at most kDecodeMaxGroups
+// groups), zero before the first call; the partial area follows at that
+// fixed offset, whatever the shape, so calls of different shapes can share a
+// workspace.  check_decode_fused checks the partial area as check_decode
+// does, plus the counter area itself.
+constexpr int kDecodeArriveBytes = 65536;
+constexpr int kDecodeMaxGroups = kDecodeArriveBytes / 4;
 int check_decode_fused(const DecodeShape& s, bool* noop);
 size_t decode_fused_workspace_size(int B, int H_q, int S_k, int D);
 int check_bwd(const BwdShape& s, bool* noop);

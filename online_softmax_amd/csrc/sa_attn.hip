@@ -74,53 +74,15 @@ void dispatch_decode(const DecArgs& args, const MergeArgs& margs, int nwg, bool 
   hipLaunchKernelGGL((decode_merge_kernel<T, D>), dim3(args.B * args.H_q * (D / 16)), dim3(256), 0, st, margs);
 }
 
-// Workgroups of the single-kernel decode instance that one CU keeps resident
-// (queried once per device).
-template <class T, int D, bool M, bool A>
-int coop_per_cu(int* out) {
-  static std::once_flag flags[kMaxDevices];
-  static int per_cu[kMaxDevices];
-  static hipError_t errs[kMaxDevices];
-  int dev = 0;
-  hipError_t e = hipGetDevice(&dev);
-  if (e != hipSuccess) return fail(SA_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
-  if (dev < 0 || dev >= kMaxDevices) return fail(SA_ERR_HIP, "device index %d out of range", dev);
-  std::call_once(flags[dev], [dev] {
-    int coop = 0;
-    errs[dev] = hipDeviceGetAttribute(&coop, hipDeviceAttributeCooperativeLaunch, dev);
-    if (errs[dev] == hipSuccess && !coop) per_cu[dev] = 0;
-    else if (errs[dev] == hipSuccess)
-      errs[dev] = hipOccupancyMaxActiveBlocksPerMultiprocessor(
-          &per_cu[dev], reinterpret_cast<const void*>(&decode_kernel<T, D, M, A, true>), 256, 0);
-  });
-  if (errs[dev] != hipSuccess) return fail(SA_ERR_HIP, "occupancy query: %s", hipGetErrorString(errs[dev]));
-  *out = per_cu[dev];
-  return SA_OK;
-}
-
 template <class T, int D>
-int coop_capacity(bool mask, bool alibi, int* per_cu) {
+void dispatch_decode_fused(const DecArgs& args, int nwg, bool mask, bool alibi, hipStream_t st) {
   const int key = (mask ? 2 : 0) | (alibi ? 1 : 0);
   switch (key) {
-    case 0: return coop_per_cu<T, D, false, false>(per_cu);
-    case 1: return coop_per_cu<T, D, false, true>(per_cu);
-    case 2: return coop_per_cu<T, D, true, false>(per_cu);
-    default: return coop_per_cu<T, D, true, true>(per_cu);
+    case 0: hipLaunchKernelGGL((decode_kernel<T, D, false, false, true>), dim3(nwg), dim3(256), 0, st, args); break;
+    case 1: hipLaunchKernelGGL((decode_kernel<T, D, false, true, true>), dim3(nwg), dim3(256), 0, st, args); break;
+    case 2: hipLaunchKernelGGL((decode_kernel<T, D, true, false, true>), dim3(nwg), dim3(256), 0, st, args); break;
+    default: hipLaunchKernelGGL((decode_kernel<T, D, true, true, true>), dim3(nwg), dim3(256), 0, st, args); break;
   }
-}
-
-template <class T, int D>
-hipError_t launch_decode_coop(DecArgs& args, int nwg, bool mask, bool alibi, hipStream_t st) {
-  void* params[] = {&args};
-  const void* f;
-  const int key = (mask ? 2 : 0) | (alibi ? 1 : 0);
-  switch (key) {
-    case 0: f = reinterpret_cast<const void*>(&decode_kernel<T, D, false, false, true>); break;
-    case 1: f = reinterpret_cast<const void*>(&decode_kernel<T, D, false, true, true>); break;
-    case 2: f = reinterpret_cast<const void*>(&decode_kernel<T, D, true, false, true>); break;
-    default: f = reinterpret_cast<const void*>(&decode_kernel<T, D, true, true, true>); break;
-  }
-  return hipLaunchCooperativeKernel(f, dim3(nwg), dim3(256), params, 0, st);
 }
 
 }  // namespace
@@ -221,8 +183,7 @@ int sa_attn_decode(const void* q, const void* k_cache, const void* v_cache, void
   args.n_hg = n_hg; args.splits = splits; args.chunk = chunk;
   args.scale2 = scale * kLog2e;
   args.alibi2 = scale != 0.f ? 1.0f / std::fabs(scale) : 0.f;
-  args.bar = nullptr;
-  args.spin_limit = 0;
+  args.arrive = nullptr;
 
   MergeArgs margs;
   margs.ws_o = args.ws_o;
@@ -261,34 +222,23 @@ int sa_attn_decode_fused(const void* q, const void* k_cache, const void* v_cache
   int cus = 0;
   st = num_cus(&cus);
   if (st != SA_OK) return st;
-  const bool m = key_padding_mask != nullptr, al = alibi_slopes != nullptr;
-  int per_cu = 0;
-  if (dtype == SA_F16) st = D == 64 ? coop_capacity<F16, 64>(m, al, &per_cu) : coop_capacity<F16, 128>(m, al, &per_cu);
-  else st = D == 64 ? coop_capacity<BF16, 64>(m, al, &per_cu) : coop_capacity<BF16, 128>(m, al, &per_cu);
-  if (st != SA_OK) return st;
-  if (per_cu <= 0) return fail(SA_ERR_UNSUPPORTED, "this device does not support cooperative launches");
-
-  // As many splits as the two-kernel decode, cut to what the device keeps
-  // resident at once (every workgroup must be resident for the barrier).
   const int G = H_q / H_kv;
   const int n_hg = (G + kDecodeHeadGroup - 1) / kDecodeHeadGroup;
-  const int64_t groups = (int64_t)B * H_kv * n_hg;
-  const int64_t resident = (int64_t)per_cu * cus;
-  if (groups > resident)
-    return fail(SA_ERR_UNSUPPORTED, "%lld head groups exceed the %lld resident workgroups of one cooperative "
-                "launch (use sa_attn_decode)", (long long)groups, (long long)resident);
-  int splits = decode_num_splits(B, S_k, H_q, H_kv, cus);
-  if (groups * splits > resident) splits = (int)(resident / groups);
+  const int splits = decode_num_splits(B, S_k, H_q, H_kv, cus);
   const int chunk = decode_chunk(S_k, splits);
-  splits = (S_k + chunk - 1) / chunk > 0 ? (S_k + chunk - 1) / chunk : 1;
+  const int64_t groups = (int64_t)B * H_kv * n_hg;
+  if (groups > kDecodeMaxGroups)
+    return fail(SA_ERR_UNSUPPORTED, "%lld head groups exceed the %d arrival counters of the workspace "
+                "(use sa_attn_decode)", (long long)groups, kDecodeMaxGroups);
   const int64_t nwg = groups * splits;
+  if (nwg > INT32_MAX) return fail(SA_ERR_INVALID_ARG, "too many decode workgroups");
   if (!decode_offsets_fit(chunk, H_kv, D))
     return fail(SA_ERR_INVALID_ARG, "one decode split would span 4 GiB or more of k_cache");
   const DecodeLayout lay = decode_layout(B, H_q, splits, D);
   if (lay.lse_offset >= ((int64_t)1 << 32))
     return fail(SA_ERR_UNSUPPORTED, "partial outputs of 4 GiB or more (use sa_attn_decode)");
 
-  char* ws = (char*)workspace + kDecodeBarrierBytes;
+  char* ws = (char*)workspace + kDecodeArriveBytes;
   DecArgs args;
   args.q = (const uint16_t*)q;
   args.k = (const uint16_t*)k_cache;
@@ -303,15 +253,16 @@ int sa_attn_decode_fused(const void* q, const void* k_cache, const void* v_cache
   args.n_hg = n_hg; args.splits = splits; args.chunk = chunk;
   args.scale2 = scale * kLog2e;
   args.alibi2 = scale != 0.f ? 1.0f / std::fabs(scale) : 0.f;
-  args.bar = (unsigned*)workspace;
-  args.spin_limit = 1 << 20;
+  args.arrive = (unsigned*)workspace;
+  const bool m = key_padding_mask != nullptr, al = alibi_slopes != nullptr;
   hipStream_t hs = (hipStream_t)stream;
-  hipError_t e;
-  if (dtype == SA_F16) e = D == 64 ? launch_decode_coop<F16, 64>(args, (int)nwg, m, al, hs)
-                                   : launch_decode_coop<F16, 128>(args, (int)nwg, m, al, hs);
-  else e = D == 64 ? launch_decode_coop<BF16, 64>(args, (int)nwg, m, al, hs)
-                   : launch_decode_coop<BF16, 128>(args, (int)nwg, m, al, hs);
-  if (e != hipSuccess) return fail(SA_ERR_HIP, "cooperative decode launch: %s", hipGetErrorString(e));
+  if (dtype == SA_F16) {
+    if (D == 64) dispatch_decode_fused<F16, 64>(args, (int)nwg, m, al, hs);
+    else dispatch_decode_fused<F16, 128>(args, (int)nwg, m, al, hs);
+  } else {
+    if (D == 64) dispatch_decode_fused<BF16, 64>(args, (int)nwg, m, al, hs);
+    else dispatch_decode_fused<BF16, 128>(args, (int)nwg, m, al, hs);
+  }
   return launched("single-kernel decode");
 }
 

@@ -134,6 +134,12 @@ def test_decode_splits_and_workspace(L):
         assert sa.decode_workspace_size(B, Hq, S, 64) >= need
     assert sa.decode_workspace_size(-1, 1, 1, 64) == 0
     assert sa.decode_workspace_size(0, 1, 1, 64) >= 0
+    # The single-kernel decode: 64 KiB of arrival counters, then the same area.
+    L = sa.lib()
+    for B, Hq, S, D in [(4, 14, 32768, 64), (1, 40, 300, 128), (0, 8, 1, 64)]:
+        assert L.sa_attn_decode_fused_workspace_size(B, Hq, S, D) == \
+            sa.DECODE_ARRIVE_BYTES + sa.decode_workspace_size(B, Hq, S, D)
+    assert L.sa_attn_decode_fused_workspace_size(-1, 1, 1, 64) == 0
 
 
 # Backward: more fake buffers beside the forward's.
