@@ -177,6 +177,11 @@ int fwd_waves(int B, int S_q, int H_q, bool causal, int num_cu) {
   return wg8 >= need ? 8 : 4;
 }
 
+int fwd_pair_ncu(int nitems, int nmb, bool causal, int nw, int num_cu) {
+  if (!causal || nw != 4 || num_cu <= 0 || nmb <= 0 || nmb % 2) return 0;
+  return (int64_t)nitems == 2 * (int64_t)num_cu ? num_cu : 0;
+}
+
 int decode_chunk(int S_k, int splits) {
   if (splits < 1) splits = 1;
   int per = (S_k + splits - 1) / splits;

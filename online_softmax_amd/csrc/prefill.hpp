@@ -77,6 +77,9 @@ struct FwdArgs {
   float alibi2;  // log2(e) / |scale log2(e)| = 1 / |scale|: bias to accumulator units
   int nmb;       // query blocks per (batch, head)
   int nitems;    // B * H_q * nmb
+  // Causal sweeps whose whole grid is resident at two workgroups per CU:
+  // the number of CUs (workgroups j and j + pair_ncu then share a CU), else 0.
+  int pair_ncu;
   const uint8_t* block_mask;  // block-sparse mode: [B, H_q, nmb, nkb], nonzero = visit
   int nkb;                    // key blocks of kSparseBlock per row of block_mask
   // Extended mode.  Bias element (b, h, i, j) at bias[b sb + h sh + i sq + j]
@@ -146,10 +149,26 @@ __global__ __launch_bounds__(NW * 64, EXT ? 1 : 2) void fwd_kernel(FwdArgs a) {
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int li = lane & 31, g = lane >> 5;
 
-  const int item = xcd_contiguous(blockIdx.x, a.nitems);
-  const int bh = item / a.nmb, mbi = item - bh * a.nmb;
-  // Causal blocks are issued heaviest (last rows) first.
-  const int mb = CAUSAL ? a.nmb - 1 - mbi : mbi;
+  int bh, mb;
+  if (CAUSAL && !SPARSE && a.pair_ncu > 0) {
+    // The whole grid is resident, two workgroups per CU, and the hardware
+    // places workgroups j and j + pair_ncu on one CU: they take blocks
+    // nmb - 1 - l and l of one head, so that every CU carries the same
+    // causal work (nmb + 1 blocks' worth); consecutive j go to different
+    // XCDs and heads repeat every B * H_q, so each XCD keeps to a few heads.
+    const int ncu = a.pair_ncu, j = blockIdx.x;
+    const int p = j < ncu ? j : j - ncu;
+    const int nbh = a.nitems / a.nmb;
+    bh = p % nbh;
+    const int lvl = p / nbh;
+    mb = j < ncu ? a.nmb - 1 - lvl : lvl;
+  } else {
+    const int item = xcd_contiguous(blockIdx.x, a.nitems);
+    bh = item / a.nmb;
+    const int mbi = item - bh * a.nmb;
+    // Causal blocks are issued heaviest (last rows) first.
+    mb = CAUSAL ? a.nmb - 1 - mbi : mbi;
+  }
   const int b = bh / a.H_q, h = bh - b * a.H_q, hk = h / a.G;
   const int m0 = mb * BM;
   const int off = a.S_k - a.S_q;  // bottom-right alignment of the causal rule

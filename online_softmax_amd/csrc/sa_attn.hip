@@ -121,6 +121,7 @@ int sa_attn_fwd(const void* q, const void* k, const void* v, void* out, float* l
   args.alibi2 = 1.0f / std::fabs(scale);
   args.nmb = (S_q + 32 * nw - 1) / (32 * nw);
   args.nitems = B * H_q * args.nmb;
+  args.pair_ncu = fwd_pair_ncu(args.nitems, args.nmb, causal != 0, nw, cus);
   args.block_mask = nullptr;
   args.nkb = 0;
   const bool c = causal != 0, m = key_padding_mask != nullptr, al = alibi_slopes != nullptr;

@@ -104,6 +104,29 @@ def test_config3_sampled(name):
     check(make_inputs(w), rows=_sample_rows(w.S_q, 24, 3), what=name)
 
 
+def test_causal_grid_every_row_written():
+    """c3 causal at full size (one resident grid of 512 four-wave workgroups
+    on a 256-CU device, where the paired block mapping applies): every row of
+    out and lse is written, starting from NaN."""
+    w = WORKLOADS["c3_causal_4096"]
+    q, k, v, _, _ = to_dev(make_inputs(w))
+    out = torch.full_like(q, float("nan"))
+    lse = torch.full((w.B, w.H_q, w.S_q), float("nan"), dtype=torch.float32, device="cuda")
+    sa.attn_fwd(q, k, v, causal=True, scale=w.scale, out=out, lse=lse)
+    torch.cuda.synchronize()
+    assert torch.isfinite(out).all() and torch.isfinite(lse).all()
+
+
+def test_causal_paired_grid_full():
+    """A causal grid of exactly two four-wave workgroups per CU on a 256-CU
+    device (B * H_q * 4 blocks = 512), checked in full."""
+    ncu = torch.cuda.get_device_properties(0).multi_processor_count
+    w = Workload("paired_grid", 2, 512, 512, 64, 8, 64, "fp16", causal=True, seed=131)
+    print(f"[fwd] paired mapping {'applies' if 2 * 64 * 4 == 2 * ncu else 'does not apply'} ({ncu} CUs)",
+          flush=True)
+    check(make_inputs(w), what=w.name)
+
+
 def test_config5_sampled():
     w = WORKLOADS["c5_alibi_8192"]
     inp = make_inputs(w)
