@@ -48,6 +48,9 @@ struct BwdArgs {
   float alibi2;         // 1 / |scale|
   int nqb;              // query blocks of 128 rows per (batch, head)   (dq kernel)
   int nkb;              // key blocks of 128 keys per (batch, KV head)  (dk/dv kernel)
+  // dq kernel: the number of CUs when its causal grid is resident at two
+  // workgroups per CU (workgroups j and j + pair_ncu share a CU), else 0.
+  int pair_ncu;
 };
 
 template <int D>
@@ -96,9 +99,22 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int li = lane & 31, g = lane >> 5;
-  const int item = xcd_contiguous(blockIdx.x, a.B * a.H_q * a.nqb);
-  const int bh = item / a.nqb, mbi = item - bh * a.nqb;
-  const int mb = CAUSAL ? a.nqb - 1 - mbi : mbi;  // heaviest blocks first
+  int bh, mb;
+  if (CAUSAL && a.pair_ncu > 0) {
+    // As in the forward: workgroups j and j + pair_ncu share a CU and take
+    // blocks nqb - 1 - l and l of one head.
+    const int ncu = a.pair_ncu, j = blockIdx.x;
+    const int p = j < ncu ? j : j - ncu;
+    const int nbh = a.B * a.H_q;
+    bh = p % nbh;
+    const int lvl = p / nbh;
+    mb = j < ncu ? a.nqb - 1 - lvl : lvl;
+  } else {
+    const int item = xcd_contiguous(blockIdx.x, a.B * a.H_q * a.nqb);
+    bh = item / a.nqb;
+    const int mbi = item - bh * a.nqb;
+    mb = CAUSAL ? a.nqb - 1 - mbi : mbi;  // heaviest blocks first
+  }
   const int b = bh / a.H_q, h = bh - b * a.H_q, hk = h / a.G;
   const int m0 = mb * BM;
   const int off = a.S_k - a.S_q;

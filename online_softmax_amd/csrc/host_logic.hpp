@@ -91,9 +91,10 @@ int decode_num_splits(int B, int S_k, int H_q, int H_kv, int num_cu);
 // they are used when there are enough of them to keep every CU busy (for
 // causal work, enough to balance the unequal blocks).
 int fwd_waves(int B, int S_q, int H_q, bool causal, int num_cu);
-// The dense forward's paired block mapping (FwdArgs::pair_ncu): num_cu when a
-// causal sweep of four-wave workgroups (two resident per CU) has exactly two
-// workgroups per CU and an even number of blocks per head, else 0.
+// The paired causal block mapping of the dense forward and of the backward's
+// dq kernel (pair_ncu): num_cu when a causal grid of four-wave workgroups
+// (two resident per CU) has exactly two workgroups per CU and an even number
+// of blocks per head, else 0.
 int fwd_pair_ncu(int nitems, int nmb, bool causal, int nw, int num_cu);
 // Keys per split for a split count (a multiple of kDecodeStepKeys).
 int decode_chunk(int S_k, int splits);

@@ -6,7 +6,6 @@
 #include <hip/hip_runtime.h>
 
 #include <cmath>
-#include <mutex>
 
 #include "../../include/sa_attn.h"
 #include "decode.hpp"
@@ -16,27 +15,6 @@
 
 namespace sa {
 namespace {
-
-constexpr int kMaxDevices = 64;
-
-// Compute-unit count per device, queried once.
-int num_cus(int* out) {
-  static std::once_flag flags[kMaxDevices];
-  static int cus[kMaxDevices];
-  static hipError_t errs[kMaxDevices];
-  int dev = 0;
-  hipError_t e = hipGetDevice(&dev);
-  if (e != hipSuccess) return fail(SA_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
-  if (dev < 0 || dev >= kMaxDevices) return fail(SA_ERR_HIP, "device index %d out of range", dev);
-  std::call_once(flags[dev], [dev] {
-    errs[dev] = hipDeviceGetAttribute(&cus[dev], hipDeviceAttributeMultiprocessorCount, dev);
-  });
-  if (errs[dev] != hipSuccess)
-    return fail(SA_ERR_HIP, "hipDeviceGetAttribute: %s", hipGetErrorString(errs[dev]));
-  *out = cus[dev];
-  return SA_OK;
-}
-
 
 template <class T, int D, bool C, bool M, bool A>
 void launch_fwd(const FwdArgs& args, int nw, hipStream_t st) {

@@ -84,6 +84,10 @@ int sa_attn_bwd(const void* q, const void* k, const void* v, const void* out, co
   args.alibi2 = scale != 0.f ? 1.0f / std::fabs(scale) : 0.f;
   args.nqb = (S_q + 127) / 128;
   args.nkb = (S_k + 127) / 128;
+  int cus = 0;
+  st = num_cus(&cus);
+  if (st != SA_OK) return st;
+  args.pair_ncu = fwd_pair_ncu(B * H_q * args.nqb, args.nqb, causal != 0, 4, cus);
   const bool c = causal != 0, m = key_padding_mask != nullptr, al = alibi_slopes != nullptr;
   hipStream_t hs = (hipStream_t)stream;
   if (dtype == SA_F16) {
