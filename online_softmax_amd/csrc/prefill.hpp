@@ -142,6 +142,7 @@ __global__ __launch_bounds__(NW * 64, EXT ? 1 : 2) void fwd_kernel(FwdArgs a) {
   __shared__ __attribute__((aligned(1024))) uint16_t Ks[NS][BN * D];
   __shared__ __attribute__((aligned(1024))) uint16_t Vs[NS][BN * D];
   __shared__ int Pw[MASK ? NW : 1];  // per-wave first cleared key
+  __shared__ int Lw[MASK ? NW : 1];  // per-wave last kept key
   __shared__ int16_t Tl[SPARSE ? kSparseMaxTiles : 1];  // block-sparse tile list
   __shared__ int Tn;                                     // its length
 
@@ -186,6 +187,59 @@ __global__ __launch_bounds__(NW * 64, EXT ? 1 : 2) void fwd_kernel(FwdArgs a) {
   const int ntd = n_end > 0 ? (n_end + BN - 1) / BN : 0;  // tiles up to the last key any row may see
   int nt = ntd;                                           // tiles the sweep visits
 
+  // The padding mask over the keys this workgroup may read (the first ntd
+  // tiles): the first key it clears (S_k if none) and the last key it keeps
+  // (-1 if none).  Tiles that end at or before the first cleared key need no
+  // padding test, the others take the masking pass (for the usual padding, a
+  // cleared tail, that is exactly the tiles holding cleared keys).  Each lane
+  // checks 16 consecutive keys per round through a buffer resource that ends
+  // at S_k (keys past it read as cleared), all 16 loads in flight together;
+  // the extremes go over the wave by shuffles and over the waves through LDS.
+  const uint8_t* mrow = MASK ? a.mask + (size_t)b * a.S_k : nullptr;
+  int pad_start = a.S_k, last_kept = -1;
+  auto mask_scan = [&]() {
+    const auto mr = buffer_rsrc_t(mrow, (uint32_t)a.S_k);
+    const int nkeys = ntd * BN;
+    int first = a.S_k, last = -1;
+    for (int j0 = 16 * (64 * w + lane); j0 < nkeys; j0 += 16 * 64 * NW) {
+      uint32_t kept[16];
+#pragma unroll
+      for (int e = 0; e < 16; ++e) kept[e] = __builtin_amdgcn_raw_buffer_load_b8(mr, (uint32_t)(j0 + e), 0, 0);
+#pragma unroll
+      for (int e = 15; e >= 0; --e) first = kept[e] == 0 ? min(first, j0 + e) : first;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) last = kept[e] != 0 ? max(last, j0 + e) : last;
+    }
+#pragma unroll
+    for (int k = 32; k > 0; k >>= 1) {
+      first = min(first, __shfl_xor(first, k));
+      last = max(last, __shfl_xor(last, k));
+    }
+    if (lane == 0) {
+      Pw[w] = first;
+      Lw[w] = last;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int x = 0; x < NW; ++x) {
+      pad_start = min(pad_start, Pw[x]);
+      last_kept = max(last_kept, Lw[x]);
+    }
+    pad_start = __builtin_amdgcn_readfirstlane(pad_start);
+    last_kept = __builtin_amdgcn_readfirstlane(last_kept);
+  };
+  // With ALiBi under the causal rule the sweep starts on its last tiles (see
+  // the sweep order below), so it ends at the last kept key: the tiles after
+  // it are cleared throughout and contribute nothing, and the first tiles
+  // taken then carry the largest biases that count, so the running maximum
+  // settles at once.  (Starting on cleared tiles instead, the maximum was
+  // first set far from the diagonal and then raised on nearly every tile.)
+  constexpr bool BAND = CAUSAL && ALIBI && !SPARSE;
+  if constexpr (MASK && BAND) {
+    mask_scan();
+    nt = min(nt, last_kept >= 0 ? last_kept / BN + 1 : 0);
+  }
+
   // Block-sparse mode: the selected tiles of this query block in key order.
   // Wave 0 takes 64 key blocks per round, one per lane; a selected block
   // contributes its one or two tiles below ntd, placed by two ballots.
@@ -213,7 +267,6 @@ __global__ __launch_bounds__(NW * 64, EXT ? 1 : 2) void fwd_kernel(FwdArgs a) {
   const size_t rs = (size_t)a.H_kv * D;  // key/value row stride
   const uint16_t* kb = a.k + ((size_t)b * a.S_k * a.H_kv + hk) * D;
   const uint16_t* vb = a.v + ((size_t)b * a.S_k * a.H_kv + hk) * D;
-  const uint8_t* mrow = MASK ? a.mask + (size_t)b * a.S_k : nullptr;
 
   // Copy u of this wave fills LDS bytes [cb KiB, cb KiB + 1 KiB) of a buffer,
   // cb = NW u + w; lane l's 16 bytes are LDS row r, position p, holding global
@@ -237,7 +290,6 @@ __global__ __launch_bounds__(NW * 64, EXT ? 1 : 2) void fwd_kernel(FwdArgs a) {
   // the steeper slopes); and the workgroups of one head still walk the shared
   // tiles from key 0 together, which keeps them in L2.  Otherwise the order
   // is plain 0 .. nt-1.
-  constexpr bool BAND = CAUSAL && ALIBI && !SPARSE;
   const int nb = BAND ? min(nt, BM / BN) : 0;
   auto tile_of = [&](int it) -> int {
     if constexpr (SPARSE) return __builtin_amdgcn_readfirstlane((int)Tl[it]);
@@ -283,34 +335,7 @@ __global__ __launch_bounds__(NW * 64, EXT ? 1 : 2) void fwd_kernel(FwdArgs a) {
     }
   }
 
-  // The first key the padding mask clears among the keys this workgroup may
-  // read (S_k if none): tiles that end at or before it need no padding test,
-  // the others take the masking pass (for the usual padding, a cleared tail,
-  // that is exactly the tiles holding cleared keys).  Each lane checks 16
-  // consecutive keys per round through a buffer resource that ends at S_k
-  // (keys past it read 0 and only push the minimum to S_k or beyond), all 16
-  // loads in flight together; the minimum goes over the wave by shuffles and
-  // over the waves through LDS.
-  int pad_start = a.S_k;
-  if (MASK) {
-    const auto mr = buffer_rsrc_t(mrow, (uint32_t)a.S_k);
-    const int nkeys = ntd * BN;
-    int first = a.S_k;
-    for (int j0 = 16 * (64 * w + lane); j0 < nkeys; j0 += 16 * 64 * NW) {
-      uint32_t kept[16];
-#pragma unroll
-      for (int e = 0; e < 16; ++e) kept[e] = __builtin_amdgcn_raw_buffer_load_b8(mr, (uint32_t)(j0 + e), 0, 0);
-#pragma unroll
-      for (int e = 15; e >= 0; --e) first = kept[e] == 0 ? min(first, j0 + e) : first;
-    }
-#pragma unroll
-    for (int k = 32; k > 0; k >>= 1) first = min(first, __shfl_xor(first, k));
-    if (lane == 0) Pw[w] = first;
-    __syncthreads();
-#pragma unroll
-    for (int x = 0; x < NW; ++x) pad_start = min(pad_start, Pw[x]);
-    pad_start = __builtin_amdgcn_readfirstlane(pad_start);
-  }
+  if constexpr (MASK && !BAND) mask_scan();
 
   float m_ref = kNegInf;  // reference maximum, base-2 domain (raised lazily)
   float l_run = 0.f;      // this lane's share of the running row sum

@@ -10,7 +10,7 @@ import pytest
 import torch
 
 import online_softmax_amd as sa
-from parity import assert_lse_close, assert_out_close, oracle_for, to_dev
+from parity import OUT_ATOL, assert_lse_close, assert_out_close, half_ulp, oracle_for, to_dev
 from workloads import WORKLOADS, Workload, make_inputs, to_f64
 
 pytestmark = pytest.mark.gpu
@@ -161,6 +161,43 @@ def test_fully_masked_rows():
     w2 = Workload("early_rows", 1, 200, 50, 2, 2, 64, "fp16", causal=True, seed=32)
     out2, lse2 = check(make_inputs(w2), what="rows before the first key")
     assert (out2[0, :150] == 0).all() and np.isneginf(lse2[0, :, :150]).all()
+
+
+@pytest.mark.parametrize("D,dt", [(128, "bf16"), (64, "fp16")])
+def test_alibi_causal_mask_patterns(D, dt):
+    """Causal ALiBi with masks other than a tail: the sweep ends at each
+    workgroup's last kept key (the tiles after it are cleared throughout), so
+    a cleared run followed by kept keys, scattered keys, a long cleared tail
+    and a batch row with every key cleared must all match the oracle.
+
+    Batch row 1 keeps only 7 scattered keys, so its rows average at most 7
+    values: the rounding of each probability to the input type before P.V
+    (relative 2^-9 in bf16, 2^-12 in fp16) no longer averages out, and that
+    row is held to 5e-3 + half an ulp + u * max|v| with u the probability
+    rounding (the derivation used for dropout); the other rows to the plain
+    bound."""
+    w = Workload(f"alibi_mask_patterns_{D}", 4, 700, 700, 4, 2, D, dt, causal=True, alibi=True, seed=33 + D)
+    inp = make_inputs(w)
+    m = torch.ones((4, 700), dtype=torch.uint8)
+    m[0, 100:300] = 0                                      # a cleared run, kept keys after it
+    m[1, :] = 0
+    m[1, torch.tensor([5, 64, 65, 130, 257, 511, 600])] = 1  # scattered kept keys
+    m[2, 41:] = 0                                          # a long cleared tail
+    m[3, :] = 0                                            # every key cleared
+    inp.mask = m
+    print(f"[fwd] {w.name} causal ALiBi, four mask patterns", flush=True)
+    out, lse = run_fwd(inp)
+    ref_o, ref_l = oracle_for(inp)
+    tdt = torch.float16 if dt == "fp16" else torch.bfloat16
+    many = [0, 2, 3]
+    assert_out_close(out[many], ref_o[many], tdt, w.name)
+    assert_lse_close(lse, ref_l, w.name)
+    u = 2.0 ** -9 if dt == "bf16" else 2.0 ** -12
+    vmax = float(to_f64(inp.v[1]).__abs__().max())
+    bound = OUT_ATOL + half_ulp(ref_o[1], tdt) + u * vmax
+    assert np.isfinite(out[1]).all() and (np.abs(out[1] - ref_o[1]) <= bound).all()
+    assert (out[3] == 0).all() and np.isneginf(lse[3]).all()
+    assert np.isneginf(lse[2, :, :41]).sum() == 0
 
 
 def test_single_key_bitwise():
