@@ -95,6 +95,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
   constexpr int NI = BN * D * 2 / 1024 / NW;  // 1 KiB copies per wave per tensor per tile
   __shared__ __attribute__((aligned(1024))) uint16_t Ks[NS][BN * D];
   __shared__ __attribute__((aligned(1024))) uint16_t Vs[NS][BN * D];
+  __shared__ int Pw[MASK ? NW : 1];  // per-wave first cleared key
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -170,6 +171,34 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
   }
   const float sc2 = a.scale2;
   const float slope_acc = ALIBI ? a.slopes[h] * a.alibi2 : 0.f;
+  // The first key the padding mask clears among the keys of the sweep (S_k
+  // if none): only tiles reaching it read mask bytes.  Each lane checks 16
+  // consecutive keys per round, all loads in flight together; the minimum
+  // goes over the wave by shuffles and over the waves through LDS.
+  int pad_start = a.S_k;
+  if (MASK) {
+    const auto mr = buffer_rsrc_t(mrow, (uint32_t)a.S_k);
+    int first = a.S_k;
+    for (int j0 = 16 * (64 * w + lane); j0 < nt * BN; j0 += 16 * 64 * NW) {
+      uint32_t kept[16];
+#pragma unroll
+      for (int e = 0; e < 16; ++e) kept[e] = __builtin_amdgcn_raw_buffer_load_b8(mr, (uint32_t)(j0 + e), 0, 0);
+#pragma unroll
+      for (int e = 15; e >= 0; --e) first = kept[e] == 0 ? min(first, j0 + e) : first;
+    }
+#pragma unroll
+    for (int k = 32; k > 0; k >>= 1) first = min(first, __shfl_xor(first, k));
+    if (lane == 0) Pw[w] = first;
+    __syncthreads();
+#pragma unroll
+    for (int x = 0; x < NW; ++x) pad_start = min(pad_start, Pw[x]);
+    pad_start = __builtin_amdgcn_readfirstlane(pad_start);
+  }
+  // Everything read into registers above has landed before the sweep.  The
+  // tile copies are inline assembly the compiler does not count, so a wait
+  // it placed inside the loop for these loads would wait for the copies in
+  // flight too.
+  wait_vmem();
   const int wrow0 = m0 + 32 * w;
   const int wave_last = min(wrow0 + 31, a.S_q - 1) + off;
   int ntw = wrow0 < a.S_q ? nt : 0;
@@ -230,12 +259,13 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
           s[jb] = T::mma(*(const u32x4*)&kt[off16], qreg[kk], s[jb]);
           dp[jb] = T::mma(*(const u32x4*)&vt[off16], doreg[kk], dp[jb]);
         }
+      const bool padded = MASK && n0 + BN > pad_start;
       const bool masked = n0 + BN > a.S_k || (CAUSAL && n0 + BN - 1 > wrow0 + off) || MASK;
       // Padding bits of the tile's 64 keys (the same for every row): lane l
       // reads the byte of key n0 + l, one ballot gathers them (bit l kept),
       // shifted to this lane's half (keys from 4 g on).
       uint64_t keep = ~uint64_t(0);
-      if (MASK) {
+      if (padded) {
         const int kl = n0 + lane;
         const bool kept = kl < a.S_k && mrow[kl < a.S_k ? kl : 0] != 0;
         keep = __builtin_amdgcn_ballot_w64(kept) >> (4 * g);
@@ -366,6 +396,11 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a) {
       vreg[kk] = kvalid ? *(const u32x4*)(a.v + rowk + 16 * kk) : (u32x4){0, 0, 0, 0};
     }
   }
+  // These rows (and the mask byte above) have landed before the sweep: the
+  // tile copies are inline assembly the compiler does not count, so a wait
+  // it placed inside the loop for these loads would wait for the copies in
+  // flight too.
+  wait_vmem();
   const float sc2 = a.scale2;
   const int kw0 = k0 + 32 * w;  // first key of this wave
 
@@ -388,6 +423,9 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a) {
     }
   const int rsw = bwd_swizzle<D>(li);
 
+  // ALiBi slope of the tile's query head, read when the head changes.
+  int slope_head = -1;
+  float slope_acc = 0.f;
   if (niter > 0) issue(0);
   for (int it = 0; it < niter; ++it) {
     if (it + 1 < niter) {
@@ -408,7 +446,10 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a) {
       const uint16_t* qt_ = Qs[it % NS];
       const uint16_t* ot_ = Os[it % NS];
       const float2* lt = Ls[it % NS];
-      const float slope_acc = ALIBI ? a.slopes[h] * a.alibi2 : 0.f;
+      if (ALIBI && gi != slope_head) {
+        slope_head = gi;
+        slope_acc = scalar_load_f32(a.slopes + __builtin_amdgcn_readfirstlane(h)) * a.alibi2;
+      }
       // S = Q K^T and dP = dO V^T for rows i0 + 8 (r/4) + 4 g + r%4 and key kj.
       f32x16 s, dp = (f32x16){};
       if (ALIBI) {

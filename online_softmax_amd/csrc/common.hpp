@@ -127,6 +127,17 @@ __device__ inline void load_lds16(i32x4 rsrc, const void* lds, uint32_t voffset)
                    :: "s"(lds_addr), "v"(voffset), "s"(rsrc) : "m0");
 }
 
+// A 32-bit load through the scalar data cache from a wave-uniform address,
+// awaited in the same statement.  Unlike a vector load it is counted apart
+// from the vector-memory operations (the LDS-destination copies above are
+// among those, and the compiler does not see them), so waiting for it never
+// waits for copies in flight.
+__device__ inline float scalar_load_f32(const float* p) {
+  float v;
+  __asm__ volatile("s_load_dword %0, %1, 0x0\n\ts_waitcnt lgkmcnt(0)" : "=s"(v) : "s"(p) : "memory");
+  return v;
+}
+
 // The same resource in the form the buffer-load builtins take.
 __device__ inline __amdgpu_buffer_rsrc_t buffer_rsrc_t(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, 0x00020000);
