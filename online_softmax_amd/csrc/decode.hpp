@@ -83,6 +83,7 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(DecArgs a) {
   constexpr int MBYTES = 3 * (2 + D) * 16 * 4;
   constexpr int SBYTES = VBYTES > MBYTES ? VBYTES : MBYTES;
   __shared__ __attribute__((aligned(1024))) unsigned char smem[SBYTES];
+  __shared__ __attribute__((aligned(1024))) uint16_t Qsh[kDecodeHeadGroup * D];  // the group's query rows
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -106,17 +107,21 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(DecArgs a) {
   const int ipos = a.S_k - 1;  // the query's position on the key axis
 
   // Q^T as the B operand: lane (column li, quarter g4) holds q[li][8 g4 + 32 kk .. +7].
+  // The group's query rows (contiguous, g_heads * D values) are copied into
+  // LDS by wave 0 ahead of its first loads of K and V, and read after those
+  // loads are all issued (see the first round below): loaded into registers
+  // here, they would have been awaited (for the sign flip) before any K/V
+  // load left, and every split would have started its stream one memory
+  // round trip late.
   const uint32_t qflip = a.scale2 < 0.f ? 0x80008000u : 0u;
   const float sc2 = __builtin_fabsf(a.scale2);
-  u32x4 qreg[KK];
-  {
-    const uint16_t* qp = a.q + ((size_t)b * a.H_q + (hvalid ? h : 0)) * D + 8 * g4;
+  constexpr int NQ = kDecodeHeadGroup * D * 2 / 1024;  // 1 KiB copies of the query rows
+  if (w == 0) {
+    const i32x4 rq = buffer_rsrc(a.q + ((size_t)b * a.H_q + h0) * D, (uint32_t)(g_heads * D * 2));
 #pragma unroll
-    for (int kk = 0; kk < KK; ++kk) {
-      qreg[kk] = hvalid ? *(const u32x4*)(qp + 32 * kk) : (u32x4){0, 0, 0, 0};
-      qreg[kk] ^= qflip;
-    }
+    for (int c = 0; c < NQ; ++c) load_lds16(rq, Qsh + c * 512, (uint32_t)(c * 1024 + 16 * lane));
   }
+  u32x4 qreg[KK];
 
   // One buffer resource per split: rows past k1 read as zero.
   const size_t rs = (size_t)a.H_kv * D;  // key/value row stride (16-bit words)
@@ -177,6 +182,15 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(DecArgs a) {
     }
     // Keep every load of the round ahead of the first wait for one of them.
     __builtin_amdgcn_sched_barrier(0);
+    if (rd == 0) {
+      // Wave 0's query copies were issued before its loads of this round;
+      // once only those loads are in flight they have landed.  The barrier
+      // does not wait for any wave's loads.
+      if (w == 0) wait_vmem_upto(NSUB * NV + NSUB * NK);
+      __builtin_amdgcn_s_barrier();
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk) qreg[kk] = *(const u32x4*)&Qsh[li * D + 8 * g4 + 32 * kk] ^ qflip;
+    }
 #pragma unroll
     for (int v = 0; v < NSUB; ++v) {
       // Sub-tiles past the split's end are computed too (their keys read as
