@@ -96,6 +96,15 @@ struct FwdArgs {
 // Philox4x32-10 (Salmon, Moraes, Dror and Shaw, "Parallel random numbers: as
 // easy as 1, 2, 3", SC'11): ten rounds over a 128-bit counter with a 64-bit
 // key, the key bumped by the two Weyl constants between rounds.
+// a ^ b ^ c in one instruction (the three-input bitwise operation with the
+// truth table of a three-way exclusive or; the compiler leaves this chain as
+// two two-input ones).
+__device__ __attribute__((always_inline)) inline uint32_t xor3(uint32_t a, uint32_t b, uint32_t c) {
+  uint32_t r;
+  __asm__("v_bitop3_b32 %0, %1, %2, %3 bitop3:0x96" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
+
 __device__ __attribute__((always_inline)) inline u32x4 philox4x32_10(uint32_t c0, uint32_t c1, uint32_t c2, uint32_t c3,
                                       uint32_t k0, uint32_t k1) {
   // The whole generator runs in vector registers, its key schedule
@@ -110,7 +119,7 @@ __device__ __attribute__((always_inline)) inline u32x4 philox4x32_10(uint32_t c0
       k1 += 0xBB67AE85u;
     }
     const uint64_t p0 = (uint64_t)0xD2511F53u * c0, p1 = (uint64_t)0xCD9E8D57u * c2;
-    const uint32_t n0 = (uint32_t)(p1 >> 32) ^ c1 ^ k0, n2 = (uint32_t)(p0 >> 32) ^ c3 ^ k1;
+    const uint32_t n0 = xor3((uint32_t)(p1 >> 32), c1, k0), n2 = xor3((uint32_t)(p0 >> 32), c3, k1);
     c1 = (uint32_t)p1;
     c3 = (uint32_t)p0;
     c0 = n0;
