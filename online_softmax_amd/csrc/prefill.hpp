@@ -94,8 +94,18 @@ struct FwdArgs {
 };
 
 // Philox4x32-10 (Salmon, Moraes, Dror and Shaw, "Parallel random numbers: as
-// easy as 1, 2, 3", SC'11): ten rounds over a 128-bit counter with a 64-bit
-// key, the key bumped by the two Weyl constants between rounds.
+// easy as 1, 2, 3", SC'11): ten rounds over a 128-bit counter (c0, c1, c2,
+// c3) with a 64-bit key (k0, k1), the key bumped by the two Weyl constants
+// between rounds; a round maps the counter to (hi(M1 c2) ^ c1 ^ k0, lo(M1 c2),
+// hi(M0 c0) ^ c3 ^ k1, lo(M0 c0)).
+//
+// The dropout counters of one lane differ only in c0 (the key quarter): c1
+// (the row), c2 (batch and head) and c3 (the offset) are fixed, so the part
+// of round 0 that does not involve c0, and the round keys, are computed once
+// per lane (PhiloxLane) and each block runs round 0 with one product.
+constexpr uint32_t kPhiloxM0 = 0xD2511F53u, kPhiloxM1 = 0xCD9E8D57u;
+constexpr uint32_t kPhiloxW0 = 0x9E3779B9u, kPhiloxW1 = 0xBB67AE85u;
+
 // a ^ b ^ c in one instruction (the three-input bitwise operation with the
 // truth table of a three-way exclusive or; the compiler leaves this chain as
 // two two-input ones).
@@ -105,27 +115,45 @@ __device__ __attribute__((always_inline)) inline uint32_t xor3(uint32_t a, uint3
   return r;
 }
 
-__device__ __attribute__((always_inline)) inline u32x4 philox4x32_10(uint32_t c0, uint32_t c1, uint32_t c2, uint32_t c3,
-                                      uint32_t k0, uint32_t k1) {
-  // The whole generator runs in vector registers, its key schedule
-  // recomputed at every call (two adds a round): hoisted as scalars out of
-  // the caller's loop it would hold twenty scalar registers the kernel does
-  // not have to spare.
-  __asm__ volatile("" : "+v"(k0), "+v"(k1));
+struct PhiloxLane {
+  uint32_t a0, b0, c0x;     // round 0: hi(M1 c2) ^ c1 ^ k0, lo(M1 c2), c3 ^ k1
+  uint32_t k0[9], k1[9];    // keys of rounds 1 .. 9
+};
+
+__device__ __attribute__((always_inline)) inline PhiloxLane philox_lane(uint32_t c1, uint32_t c2, uint32_t c3,
+                                                                       uint32_t k0, uint32_t k1) {
+  PhiloxLane p;
+  const uint64_t p1 = (uint64_t)kPhiloxM1 * c2;
+  p.a0 = (uint32_t)(p1 >> 32) ^ c1 ^ k0;
+  p.b0 = (uint32_t)p1;
+  p.c0x = c3 ^ k1;
 #pragma unroll
-  for (int r = 0; r < 10; ++r) {
-    if (r) {
-      k0 += 0x9E3779B9u;
-      k1 += 0xBB67AE85u;
-    }
-    const uint64_t p0 = (uint64_t)0xD2511F53u * c0, p1 = (uint64_t)0xCD9E8D57u * c2;
-    const uint32_t n0 = xor3((uint32_t)(p1 >> 32), c1, k0), n2 = xor3((uint32_t)(p0 >> 32), c3, k1);
-    c1 = (uint32_t)p1;
-    c3 = (uint32_t)p0;
-    c0 = n0;
-    c2 = n2;
+  for (int r = 1; r < 10; ++r) {
+    p.k0[r - 1] = k0 + (uint32_t)r * kPhiloxW0;
+    p.k1[r - 1] = k1 + (uint32_t)r * kPhiloxW1;
   }
-  return (u32x4){c0, c1, c2, c3};
+  // Keep the lane constants in vector registers (as scalars they would take
+  // about twenty scalar registers the kernel does not have to spare).
+  __asm__ volatile("" : "+v"(p.a0), "+v"(p.b0), "+v"(p.c0x));
+#pragma unroll
+  for (int r = 0; r < 9; ++r) __asm__ volatile("" : "+v"(p.k0[r]), "+v"(p.k1[r]));
+  return p;
+}
+
+// The block of counter (c0, c1, c2, c3) of the lane constants L.
+__device__ __attribute__((always_inline)) inline u32x4 philox4x32_10(uint32_t c0, const PhiloxLane& L) {
+  const uint64_t q0 = (uint64_t)kPhiloxM0 * c0;
+  uint32_t x0 = L.a0, x1 = L.b0, x2 = (uint32_t)(q0 >> 32) ^ L.c0x, x3 = (uint32_t)q0;
+#pragma unroll
+  for (int r = 0; r < 9; ++r) {
+    const uint64_t p0 = (uint64_t)kPhiloxM0 * x0, p1 = (uint64_t)kPhiloxM1 * x2;
+    const uint32_t n0 = xor3((uint32_t)(p1 >> 32), x1, L.k0[r]), n2 = xor3((uint32_t)(p0 >> 32), x3, L.k1[r]);
+    x1 = (uint32_t)p1;
+    x3 = (uint32_t)p0;
+    x0 = n0;
+    x2 = n2;
+  }
+  return (u32x4){x0, x1, x2, x3};
 }
 
 // Chunk swizzle of LDS row r (16-byte chunks, D / 8 per row).
@@ -188,6 +216,11 @@ __global__ __launch_bounds__(NW * 64, EXT ? 1 : 2) void fwd_kernel(FwdArgs a) {
   // Extended mode: this lane's bias row and whether dropout is on.
   const bool has_bias = EXT && a.bias != nullptr;
   const bool dropping = EXT && a.drop_thr != 0u;
+  // Dropout: this lane's generator constants (its row and head are fixed).
+  PhiloxLane plane{};
+  if constexpr (EXT) {
+    if (dropping) plane = philox_lane((uint32_t)qi, (uint32_t)bh, a.drop_offset, a.seed_lo, a.seed_hi);
+  }
   const float* brow_bias =
       has_bias && qi < a.S_q ? a.bias + b * a.bias_sb + h * a.bias_sh + qi * a.bias_sq : nullptr;
 
@@ -507,8 +540,7 @@ __global__ __launch_bounds__(NW * 64, EXT ? 1 : 2) void fwd_kernel(FwdArgs a) {
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
       const int j0 = n0 + 32 * (u >> 2) + 8 * (u & 3) + 4 * g;
-      const u32x4 wd = philox4x32_10((uint32_t)(j0 >> 2), (uint32_t)qi, (uint32_t)bh, a.drop_offset,
-                                     a.seed_lo, a.seed_hi);
+      const u32x4 wd = philox4x32_10((uint32_t)(j0 >> 2), plane);
 #pragma unroll
       for (int e = 0; e < 4; ++e) bits |= (wd[e] >= a.drop_thr ? 1u : 0u) << (16 * (u >> 2) + 4 * (u & 3) + e);
     }
