@@ -44,7 +44,8 @@
 //    of 4 waves owns one block of 128 query rows and sweeps only the key
 //    blocks of 128 that its row of the block mask selects; wave 0 compacts
 //    the selected 64-key tiles into a list in LDS, and the sweep walks that
-//    list in key order with everything else unchanged;
+//    list in key order (under causal ALiBi from its last tile down, for the
+//    reason given for the band order) with everything else unchanged;
 //  * extended mode (the additive masks and Philox dropout of the
 //    "StreamAttention" page, "Recent Updates"): an additive float32 bias is
 //    loaded for each tile while the previous tile's matrix work runs and is
@@ -277,23 +278,26 @@ __global__ __launch_bounds__(NW * 64, EXT ? 1 : 2) void fwd_kernel(FwdArgs a) {
   // settles at once.  (Starting on cleared tiles instead, the maximum was
   // first set far from the diagonal and then raised on nearly every tile.)
   constexpr bool BAND = CAUSAL && ALIBI && !SPARSE;
-  if constexpr (MASK && BAND) {
+  // Sweeps that start on their last tiles: the dense band order above, and
+  // in block-sparse mode the whole selected list from its last tile down.
+  constexpr bool DESC = CAUSAL && ALIBI;
+  if constexpr (MASK && DESC) {
     mask_scan();
     nt = min(nt, last_kept >= 0 ? last_kept / BN + 1 : 0);
   }
 
   // Block-sparse mode: the selected tiles of this query block in key order.
   // Wave 0 takes 64 key blocks per round, one per lane; a selected block
-  // contributes its one or two tiles below ntd, placed by two ballots.
+  // contributes its one or two tiles below nt, placed by two ballots.
   if constexpr (SPARSE) {
     if (w == 0) {
       const uint8_t* brow = a.block_mask + ((size_t)bh * a.nmb + mb) * a.nkb;
-      const int nkv = (ntd + 1) / 2;  // key blocks holding a tile below ntd
+      const int nkv = (nt + 1) / 2;  // key blocks holding a tile below nt
       int base = 0;
       for (int kb0 = 0; kb0 < nkv; kb0 += 64) {
         const int kbl = kb0 + lane;
         const bool sel = kbl < nkv && brow[kbl < nkv ? kbl : 0] != 0;
-        const bool two = sel && 2 * kbl + 1 < ntd;
+        const bool two = sel && 2 * kbl + 1 < nt;
         const uint64_t bs = __builtin_amdgcn_ballot_w64(sel), bt = __builtin_amdgcn_ballot_w64(two);
         const int pos = base + lanes_below(bs, lane) + lanes_below(bt, lane);
         if (sel) Tl[pos] = (int16_t)(2 * kbl);
@@ -334,7 +338,7 @@ __global__ __launch_bounds__(NW * 64, EXT ? 1 : 2) void fwd_kernel(FwdArgs a) {
   // is plain 0 .. nt-1.
   const int nb = BAND ? min(nt, BM / BN) : 0;
   auto tile_of = [&](int it) -> int {
-    if constexpr (SPARSE) return __builtin_amdgcn_readfirstlane((int)Tl[it]);
+    if constexpr (SPARSE) return __builtin_amdgcn_readfirstlane((int)Tl[DESC ? nt - 1 - it : it]);
     else return it < nb ? nt - 1 - it : it - nb;
   };
   auto issue_k = [&](int t) {
@@ -377,7 +381,7 @@ __global__ __launch_bounds__(NW * 64, EXT ? 1 : 2) void fwd_kernel(FwdArgs a) {
     }
   }
 
-  if constexpr (MASK && !BAND) mask_scan();
+  if constexpr (MASK && !DESC) mask_scan();
 
   float m_ref = kNegInf;  // reference maximum, base-2 domain (raised lazily)
   float l_run = 0.f;      // this lane's share of the running row sum
@@ -714,9 +718,9 @@ __global__ __launch_bounds__(NW * 64, EXT ? 1 : 2) void fwd_kernel(FwdArgs a) {
 
   // Tiles this wave needs: all of them, or under the causal rule those that
   // start at or before the wave's furthest visible key.  They are the
-  // iterations [t0w, t1w): in key order the first ntw, in band-first order
-  // the last ntw (the band tiles past the wave's diagonal come first and are
-  // the ones it skips).
+  // iterations [t0w, t1w): in key order the first ntw, in band-first (or
+  // descending) order the last ntw (the tiles past the wave's diagonal come
+  // first and are the ones it skips).
   int ntw = wave_active ? nt : 0;
   if (CAUSAL) {
     if (wave_last < 0) {
@@ -727,7 +731,7 @@ __global__ __launch_bounds__(NW * 64, EXT ? 1 : 2) void fwd_kernel(FwdArgs a) {
       int lo = 0, hi = ntw;
       while (lo < hi) {
         const int mid = (lo + hi) >> 1;
-        if (tile_of(mid) <= last_tile) lo = mid + 1;
+        if (__builtin_amdgcn_readfirstlane((int)Tl[mid]) <= last_tile) lo = mid + 1;
         else hi = mid;
       }
       ntw = lo;
@@ -735,8 +739,8 @@ __global__ __launch_bounds__(NW * 64, EXT ? 1 : 2) void fwd_kernel(FwdArgs a) {
       ntw = min(ntw, wave_last / BN + 1);
     }
   }
-  const int t0w = BAND ? nt - ntw : 0;
-  const int t1w = BAND ? nt : ntw;
+  const int t0w = DESC ? nt - ntw : 0;
+  const int t1w = DESC ? nt : ntw;
 
   // Iteration t issues K of tile t+NS (into the buffer K(t) left, whose Sᵀ
   // was formed in iteration t-1) and V of tile t+NS-1 (into the buffer of
@@ -826,7 +830,7 @@ __global__ __launch_bounds__(NW * 64, EXT ? 1 : 2) void fwd_kernel(FwdArgs a) {
   // Iteration 0 overwrites the buffer of K(0): every wave must have read it.
   __syncthreads();
   int t = 0;
-  if (BAND) {
+  if (DESC) {
     // Iterations before this wave's first tile take part in the copies and
     // barriers only.  In the last of them the wave forms Sᵀ of its first
     // tile: that K landed before the previous barrier, and its buffer is

@@ -29,19 +29,32 @@ def half_ulp(x: np.ndarray, dtype: torch.dtype) -> np.ndarray:
     return 0.5 * np.exp2(e - mant)
 
 
-def out_errors(gpu: np.ndarray, ref: np.ndarray, dtype: torch.dtype):
+def out_errors(gpu: np.ndarray, ref: np.ndarray, dtype: torch.dtype, extra=None):
     """(max abs error, count above the bound, count above 5e-3 literally)."""
     err = np.abs(np.asarray(gpu, np.float64) - ref)
-    bound = OUT_ATOL + half_ulp(ref, dtype)
+    bound = OUT_ATOL + half_ulp(ref, dtype) + (0.0 if extra is None else extra)
     return float(err.max(initial=0.0)), int((err > bound).sum()), int((err > OUT_ATOL).sum())
 
 
-def assert_out_close(gpu, ref, dtype, what=""):
+def assert_out_close(gpu, ref, dtype, what="", extra=None):
+    """``extra``: a further per-element term of the bound (see p_rounding)."""
     gpu = np.asarray(gpu, np.float64)
     assert gpu.shape == ref.shape, (gpu.shape, ref.shape)
     assert np.isfinite(gpu).all(), f"{what}: non-finite output"
-    mx, nbad, _ = out_errors(gpu, ref, dtype)
-    assert nbad == 0, f"{what}: {nbad} output elements beyond 5e-3 + half-ulp (max abs err {mx:.3e})"
+    mx, nbad, _ = out_errors(gpu, ref, dtype, extra)
+    assert nbad == 0, f"{what}: {nbad} output elements beyond the bound (max abs err {mx:.3e})"
+
+
+def p_rounding(abs_v_out, dtype):
+    """The rounding of each probability to the input type before P.V moves an
+    output by at most u * sum_j w_j |v_j| (w the row's softmax weights; u =
+    2^-9 for bfloat16, 2^-12 for float16).  Over many keys these errors
+    average out and the plain bound holds; where a row's weight sits on a few
+    keys (a steep ALiBi slope decays it by a constant factor per key, or few
+    keys are visible) they do not.  ``abs_v_out`` is the oracle's output with
+    |v| in place of v, i.e. sum_j w_j |v_j| per element."""
+    u = 2.0 ** -9 if dtype == torch.bfloat16 else 2.0 ** -12
+    return u * np.asarray(abs_v_out, np.float64)
 
 
 def assert_lse_close(gpu, ref, what=""):
