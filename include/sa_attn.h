@@ -227,6 +227,11 @@ int sa_attn_decode_fused(const void* q, const void* k_cache, const void* v_cache
  * num_cu compute units (host arithmetic only; exposed for tests and tools). */
 int sa_attn_decode_num_splits(int B, int S_k, int H_q, int H_kv, int num_cu);
 
+/* Number of key splits sa_attn_decode_fused uses: that of sa_attn_decode,
+ * capped at 64 per head group (the last split of a group merges all of the
+ * group's partial results alone), then rounded to whole 128-key steps. */
+int sa_attn_decode_fused_num_splits(int B, int S_k, int H_q, int H_kv, int num_cu);
+
 /*
  * Bytes of device workspace sa_attn_bwd needs: one float2 per (batch, query
  * head, row), B * H_q * S_q * 8.  Pure host arithmetic; 0 for a negative

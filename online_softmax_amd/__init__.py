@@ -50,6 +50,7 @@ SIGNATURES = {
     "sa_attn_decode_workspace_size": (_SZ, [_I, _I, _I, _I]),
     "sa_attn_decode": (_I, [_VP, _VP, _VP, _VP, _FP, _I, _I, _I, _I, _I, _F, _U8P, _FP, _I, _VP, _SZ, _VP]),
     "sa_attn_decode_num_splits": (_I, [_I, _I, _I, _I, _I]),
+    "sa_attn_decode_fused_num_splits": (_I, [_I, _I, _I, _I, _I]),
     "sa_attn_decode_fused_workspace_size": (_SZ, [_I, _I, _I, _I]),
     "sa_attn_decode_fused": (_I, [_VP, _VP, _VP, _VP, _FP, _I, _I, _I, _I, _I, _F, _U8P, _FP, _I, _VP, _SZ, _VP]),
     "sa_attn_bwd_workspace_size": (_SZ, [_I, _I, _I]),
@@ -263,6 +264,10 @@ def decode_workspace_size(B: int, H_q: int, S_k: int, D: int) -> int:
 
 def decode_num_splits(B: int, S_k: int, H_q: int, H_kv: int, num_cu: int) -> int:
     return int(lib().sa_attn_decode_num_splits(B, S_k, H_q, H_kv, num_cu))
+
+
+def decode_fused_num_splits(B: int, S_k: int, H_q: int, H_kv: int, num_cu: int) -> int:
+    return int(lib().sa_attn_decode_fused_num_splits(B, S_k, H_q, H_kv, num_cu))
 
 
 def decode_workspace(B: int, H_q: int, S_k: int, D: int, device) -> torch.Tensor:

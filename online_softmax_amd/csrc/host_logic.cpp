@@ -160,14 +160,23 @@ int decode_num_splits(int B, int S_k, int H_q, int H_kv, int num_cu) {
   const int G = H_q / H_kv;
   const int64_t groups = (int64_t)B * H_kv * ((G + kDecodeHeadGroup - 1) / kDecodeHeadGroup);
   const int max_splits = (int)std::min<int64_t>(kDecodeMaxSplits, (S_k + kDecodeStepKeys - 1) / kDecodeStepKeys);
-  // Aim for two four-wave workgroups per compute unit so that each CU keeps
-  // eight waves of key/value loads in flight.
-  const int64_t target = 2 * (int64_t)(num_cu > 0 ? num_cu : 1);
+  // Aim for one four-wave workgroup per compute unit.  On 32K-key caches
+  // (14:2 heads, D = 64) at batch 1, 2 and 4 this was 1-12 % faster than two
+  // per CU with half the keys each, whose partial results also double the
+  // merge's reads; a target of 1.5 per CU gave splits of 1.5 rounds and was
+  // slower than both.
+  const int64_t target = (int64_t)(num_cu > 0 ? num_cu : 1);
   int64_t splits = (target + groups - 1) / groups;
   if (splits < 1) splits = 1;
   if (splits > max_splits) splits = max_splits;
   // Round to whole steps per split, then drop splits that would be empty.
   const int chunk = decode_chunk(S_k, (int)splits);
+  return (S_k + chunk - 1) / chunk;
+}
+
+int decode_fused_num_splits(int B, int S_k, int H_q, int H_kv, int num_cu) {
+  const int splits = std::min(decode_num_splits(B, S_k, H_q, H_kv, num_cu), kDecodeFusedMaxSplits);
+  const int chunk = decode_chunk(S_k, splits);
   return (S_k + chunk - 1) / chunk;
 }
 

@@ -34,6 +34,9 @@ constexpr int kDecodeStepKeys = 128;
 constexpr int kDecodeMaxSplits = 256;
 // Query heads one decode workgroup serves at once (the MFMA column count).
 constexpr int kDecodeHeadGroup = 16;
+// Most splits per head group in the single-kernel decode, where the last
+// split of a group reads all of the group's partial results by itself.
+constexpr int kDecodeFusedMaxSplits = 64;
 // Keys a decode workgroup addresses per round (4 waves x up to 4 sub-tiles of
 // 32 keys); the last round of a split may run past its end.
 constexpr int kDecodeRoundKeys = 512;
@@ -86,6 +89,9 @@ int check_block_sparse(const FwdShape& s, const uint8_t* block_mask, bool* noop)
 size_t bwd_workspace_size(int B, int H_q, int S_q);
 
 int decode_num_splits(int B, int S_k, int H_q, int H_kv, int num_cu);
+// The split count of the single-kernel decode: decode_num_splits capped at
+// kDecodeFusedMaxSplits (then rounded to whole steps again).
+int decode_fused_num_splits(int B, int S_k, int H_q, int H_kv, int num_cu);
 // Waves per prefill workgroup (4 or 8; a workgroup owns 32 query rows per
 // wave).  Eight-wave workgroups halve the key/value copy traffic per FLOP;
 // they are used when there are enough of them to keep every CU busy (for

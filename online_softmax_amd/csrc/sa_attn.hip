@@ -122,6 +122,10 @@ int sa_attn_decode_num_splits(int B, int S_k, int H_q, int H_kv, int num_cu) {
   return sa::decode_num_splits(B, S_k, H_q, H_kv, num_cu);
 }
 
+int sa_attn_decode_fused_num_splits(int B, int S_k, int H_q, int H_kv, int num_cu) {
+  return sa::decode_fused_num_splits(B, S_k, H_q, H_kv, num_cu);
+}
+
 int sa_attn_decode(const void* q, const void* k_cache, const void* v_cache, void* out, float* lse,
                    int B, int S_k, int H_q, int H_kv, int D, float scale,
                    const uint8_t* key_padding_mask, const float* alibi_slopes, int dtype,
@@ -203,7 +207,7 @@ int sa_attn_decode_fused(const void* q, const void* k_cache, const void* v_cache
   if (st != SA_OK) return st;
   const int G = H_q / H_kv;
   const int n_hg = (G + kDecodeHeadGroup - 1) / kDecodeHeadGroup;
-  const int splits = decode_num_splits(B, S_k, H_q, H_kv, cus);
+  const int splits = decode_fused_num_splits(B, S_k, H_q, H_kv, cus);
   const int chunk = decode_chunk(S_k, splits);
   const int64_t groups = (int64_t)B * H_kv * n_hg;
   if (groups > kDecodeMaxGroups)

@@ -117,8 +117,16 @@ def test_status_strings(L):
 
 def test_decode_splits_and_workspace(L):
     # 32K keys, 4 sequences, 14:2 GQA on 256 CUs: 8 (batch, KV head) pairs,
-    # two workgroups per CU -> 64 splits of 512 keys.
-    assert sa.decode_num_splits(4, 32768, 14, 2, 256) == 64
+    # one workgroup per CU -> 32 splits of 1024 keys.
+    assert sa.decode_num_splits(4, 32768, 14, 2, 256) == 32
+    assert sa.decode_num_splits(4, 32768, 14, 2, 304) == 37  # 38 -> 863 -> 896 keys
+    # Batch 1: 2 pairs -> 128 splits of 256 keys; the single-kernel decode
+    # caps them at 64 (512 keys), and takes the same count where it is lower.
+    assert sa.decode_num_splits(1, 32768, 14, 2, 256) == 128
+    assert sa.decode_fused_num_splits(1, 32768, 14, 2, 256) == 64
+    assert sa.decode_fused_num_splits(4, 32768, 14, 2, 256) == 32
+    # 40000 keys over at most 64 splits: 625 -> 640-key splits, 63 of them.
+    assert sa.decode_fused_num_splits(1, 40000, 32, 2, 256) == 63
     # Never more splits than 128-key steps, never fewer than one.
     assert sa.decode_num_splits(1, 100, 8, 8, 256) == 1
     assert sa.decode_num_splits(1, 1000, 1, 1, 256) == 8

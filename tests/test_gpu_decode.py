@@ -133,7 +133,8 @@ FUSED_CASES = [
     Workload("fu_b1_k1", 1, 1, 1, 4, 4, 64, "fp16", decode=True, seed=61),
     # 320 head groups of two splits each
     Workload("fu_b40_groups", 40, 1, 700, 32, 8, 64, "bf16", decode=True, random_tail=300, seed=62),
-    # one group of 16 heads over 256 splits at D = 128: the merge takes 16 passes
+    # two groups of 16 heads at D = 128 over 63 splits: 512 (head, d chunk) pairs,
+    # so the merge takes two sweeps of two chunks, the second one ragged
     Workload("fu_b1_g16_d128_40k", 1, 1, 40000, 32, 2, 128, "fp16", decode=True, seed=63),
 ]
 
