@@ -164,10 +164,18 @@ __device__ inline int lds_swizzle(int r) {
   else return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);
 }
 
+// NG = 2 splits the NW waves into two groups that own the same BM = 16 NW
+// query rows: group 0 takes the sweep's tiles 0, 2, 4, ... and group 1 the
+// tiles 1, 3, 5, ... (each iteration stages one tile per group), and group 1's
+// state joins group 0's at the end.  Eight waves then cover a 128-row block
+// at two waves per SIMD, so that causal blocks of very unequal length can be
+// spread over the CUs heaviest first instead of pairing them on one CU.
 template <class T, int D, bool CAUSAL, bool MASK, bool ALIBI, int NW, bool SPARSE = false,
-          bool EXT = false>
+          bool EXT = false, int NG = 1>
 __global__ __launch_bounds__(NW * 64, EXT ? 1 : 2) void fwd_kernel(FwdArgs a) {
-  constexpr int BM = 32 * NW;        // query rows per workgroup
+  static_assert(NG == 1 || (NG == 2 && NW == 8 && !SPARSE && !EXT), "two groups: dense eight-wave kernel only");
+  constexpr int NWG = NW / NG;       // waves per group
+  constexpr int BM = 32 * NWG;       // query rows per workgroup
   constexpr int BN = 64;             // keys per tile
   constexpr int NS = 2;  // LDS buffers per tensor
   constexpr int KK = D / 16;         // MFMA k-steps over the head dimension
@@ -177,8 +185,8 @@ __global__ __launch_bounds__(NW * 64, EXT ? 1 : 2) void fwd_kernel(FwdArgs a) {
   static_assert(!SPARSE || BM == kSparseBlock, "a block-sparse workgroup owns one query block");
   static_assert(!(SPARSE && EXT), "one mode at a time");
 
-  __shared__ __attribute__((aligned(1024))) uint16_t Ks[NS][BN * D];
-  __shared__ __attribute__((aligned(1024))) uint16_t Vs[NS][BN * D];
+  __shared__ __attribute__((aligned(1024))) uint16_t Ks[NS][NG * BN * D];
+  __shared__ __attribute__((aligned(1024))) uint16_t Vs[NS][NG * BN * D];
   __shared__ int Pw[MASK ? NW : 1];  // per-wave first cleared key
   __shared__ int Lw[MASK ? NW : 1];  // per-wave last kept key
   __shared__ int16_t Tl[SPARSE ? kSparseMaxTiles : 1];  // block-sparse tile list
@@ -187,6 +195,8 @@ __global__ __launch_bounds__(NW * 64, EXT ? 1 : 2) void fwd_kernel(FwdArgs a) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int li = lane & 31, g = lane >> 5;
+  const int gw = NG == 1 ? 0 : w / NWG;  // this wave's group
+  const int wi = w - gw * NWG;           // and its place in the group
 
   int bh, mb;
   if (CAUSAL && !SPARSE && a.pair_ncu > 0) {
@@ -211,7 +221,7 @@ __global__ __launch_bounds__(NW * 64, EXT ? 1 : 2) void fwd_kernel(FwdArgs a) {
   const int b = bh / a.H_q, h = bh - b * a.H_q, hk = h / a.G;
   const int m0 = mb * BM;
   const int off = a.S_k - a.S_q;  // bottom-right alignment of the causal rule
-  const int qi = m0 + 32 * w + li;
+  const int qi = m0 + 32 * wi + li;
   const int ipos = qi + off;      // this row's position on the key axis
 
   // Extended mode: this lane's bias row and whether dropout is on.
@@ -341,26 +351,39 @@ __global__ __launch_bounds__(NW * 64, EXT ? 1 : 2) void fwd_kernel(FwdArgs a) {
     if constexpr (SPARSE) return __builtin_amdgcn_readfirstlane((int)Tl[DESC ? nt - 1 - it : it]);
     else return it < nb ? nt - 1 - it : it - nb;
   };
+  // Iteration t stages the tiles of sweep positions NG t .. NG t + NG - 1
+  // (those below nt), the one of group j at offset j BN D of the buffer.
+  const int nti = (nt + NG - 1) / NG;  // iterations of the sweep
   auto issue_k = [&](int t) {
-    const auto r = tile_rsrc(kb, tile_of(t) * BN);
-    uint16_t* buf = Ks[t % NS];
 #pragma unroll
-    for (int u = 0; u < NI; ++u) load_lds16(r, buf + (NW * u + w) * 512, voff[u]);
+    for (int j = 0; j < NG; ++j) {
+      if (NG > 1 && NG * t + j >= nt) break;
+      const auto r = tile_rsrc(kb, tile_of(NG * t + j) * BN);
+      uint16_t* buf = Ks[t % NS] + j * BN * D;
+#pragma unroll
+      for (int u = 0; u < NI; ++u) load_lds16(r, buf + (NW * u + w) * 512, voff[u]);
+    }
   };
   auto issue_v = [&](int t) {
-    const auto r = tile_rsrc(vb, tile_of(t) * BN);
-    uint16_t* buf = Vs[t % NS];
 #pragma unroll
-    for (int u = 0; u < NI; ++u) load_lds16(r, buf + (NW * u + w) * 512, voff[u]);
+    for (int j = 0; j < NG; ++j) {
+      if (NG > 1 && NG * t + j >= nt) break;
+      const auto r = tile_rsrc(vb, tile_of(NG * t + j) * BN);
+      uint16_t* buf = Vs[t % NS] + j * BN * D;
+#pragma unroll
+      for (int u = 0; u < NI; ++u) load_lds16(r, buf + (NW * u + w) * 512, voff[u]);
+    }
   };
+  // The tile this wave works on in iteration t.
+  auto wtile = [&](int t) -> int { return tile_of(NG * t + gw); };
 
-  // Prologue copies: K of tiles 0..NS-1, V of tiles 0..NS-2.
+  // Prologue copies: K of iterations 0..NS-1, V of iterations 0..NS-2.
 #pragma unroll
   for (int j = 0; j < NS; ++j)
-    if (j < nt) issue_k(j);
+    if (j < nti) issue_k(j);
 #pragma unroll
   for (int j = 0; j < NS - 1; ++j)
-    if (j < nt) issue_v(j);
+    if (j < nti) issue_v(j);
 
   // Q^T as the B operand: lane (row li, half g) holds q[row][16kk + 8g .. +7].
   // A negative scale is applied as |scale| on negated Q (exact in fp16/bf16),
@@ -391,7 +414,7 @@ __global__ __launch_bounds__(NW * 64, EXT ? 1 : 2) void fwd_kernel(FwdArgs a) {
 
   // ALiBi slope in accumulator units: bias / |scale| per unit distance.
   const float slope_acc = ALIBI ? a.slopes[h] * a.alibi2 : 0.f;
-  const int wrow0 = m0 + 32 * w;                       // first row of this wave
+  const int wrow0 = m0 + 32 * wi;                      // first row of this wave
   const bool wave_active = wrow0 < a.S_q;
   const int wave_last = min(wrow0 + 31, a.S_q - 1) + off;  // furthest key the wave may see
 
@@ -416,7 +439,7 @@ __global__ __launch_bounds__(NW * 64, EXT ? 1 : 2) void fwd_kernel(FwdArgs a) {
   // causal rule every visible key has key <= ipos, so it is linear there.
   auto init_scores = [&](const int t, const int jb, f32x16 (&s)[2]) {
     if (ALIBI) {
-      const float rel = (float)(tile_of(t) * BN + 4 * g - ipos);  // key - ipos at r = 0, jb = 0
+      const float rel = (float)(wtile(t) * BN + 4 * g - ipos);  // key - ipos at r = 0, jb = 0
       const float b0 = slope_acc * rel;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
@@ -433,7 +456,7 @@ __global__ __launch_bounds__(NW * 64, EXT ? 1 : 2) void fwd_kernel(FwdArgs a) {
     return *(const u32x4*)&kbuf[(32 * jb + li) * D + 8 * ((2 * kk + g) ^ ksw)];
   };
   auto qk = [&](const int t, f32x16 (&s)[2]) {
-    const uint16_t* kbuf = Ks[t % NS];
+    const uint16_t* kbuf = Ks[t % NS] + gw * BN * D;
     init_scores(t, 0, s);
     init_scores(t, 1, s);
 #pragma unroll
@@ -448,14 +471,14 @@ __global__ __launch_bounds__(NW * 64, EXT ? 1 : 2) void fwd_kernel(FwdArgs a) {
   // maximum is raised only when some row's tile maximum exceeds it by more
   // than the slack (rows that need no change get alpha = 1).
   auto tile_masked = [&](const int it) -> bool {
-    const int t = tile_of(it);
+    const int t = wtile(it);
     const int n0 = t * BN;
     bool masked = n0 + BN > a.S_k || (CAUSAL && n0 + BN - 1 > wrow0 + off);
     if (MASK) masked = masked || n0 + BN > pad_start;
     return masked;
   };
   auto mask_tile = [&](const int it, f32x16 (&s)[2]) {
-    const int t = tile_of(it);
+    const int t = wtile(it);
     const int n0 = t * BN;
     const bool pad_free = !MASK || n0 + BN <= pad_start;
     // The padding bits of the tile's 64 keys are the same for every row:
@@ -512,7 +535,7 @@ __global__ __launch_bounds__(NW * 64, EXT ? 1 : 2) void fwd_kernel(FwdArgs a) {
   // four consecutive keys per quarter): eight 16-byte loads per lane, scalar
   // loads for a quarter that crosses the end of the keys, zeros past it.
   auto bias_load = [&](const int it, f32x4 (&bv)[8]) {
-    const int n0 = tile_of(it) * BN;
+    const int n0 = wtile(it) * BN;
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
       const int j0 = n0 + 32 * (u >> 2) + 8 * (u & 3) + 4 * g;
@@ -539,7 +562,7 @@ __global__ __launch_bounds__(NW * 64, EXT ? 1 : 2) void fwd_kernel(FwdArgs a) {
   // r of block jb.  One generator block per quarter of four keys, counter
   // (key / 4, row, b * H_q + h, offset), word key % 4.
   auto keep_bits = [&](const int it) __attribute__((always_inline)) -> uint32_t {
-    const int n0 = tile_of(it) * BN;
+    const int n0 = wtile(it) * BN;
     uint32_t bits = 0;
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
@@ -588,7 +611,7 @@ __global__ __launch_bounds__(NW * 64, EXT ? 1 : 2) void fwd_kernel(FwdArgs a) {
 
   // Oᵀ += Vᵀ Pᵀ over four 16-key steps of tile t.
   auto pv = [&](const int t, const uint32_t (&pk)[2][8]) {
-    const uint16_t* vbuf = Vs[t % NS];
+    const uint16_t* vbuf = Vs[t % NS] + gw * BN * D;
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
       const int jb = ks >> 1, mh = ks & 1;
@@ -656,7 +679,7 @@ __global__ __launch_bounds__(NW * 64, EXT ? 1 : 2) void fwd_kernel(FwdArgs a) {
   // ahead) with pairs 0 .. EQ-1 of the current tile s.
   auto qk_exp = [&](const int t1, f32x16 (&sn)[2], const f32x16 (&s)[2], const float nm,
                     uint32_t (&pk)[2][8], float (&ps)[2], const uint32_t keep) {
-    const uint16_t* kbuf = Ks[t1 % NS];
+    const uint16_t* kbuf = Ks[t1 % NS] + gw * BN * D;
     u32x4 ak[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) ak[i] = k_frag(kbuf, i);
@@ -677,7 +700,7 @@ __global__ __launch_bounds__(NW * 64, EXT ? 1 : 2) void fwd_kernel(FwdArgs a) {
   // maximum of the next tile sn (as if no key were hidden) in two chains.
   auto pv_max = [&](const int t, const f32x16 (&s)[2], const float nm, uint32_t (&pk)[2][8],
                     float (&ps)[2], const f32x16 (&sn)[2], const uint32_t keep) -> float {
-    const uint16_t* vbuf = Vs[t % NS];
+    const uint16_t* vbuf = Vs[t % NS] + gw * BN * D;
     auto v_frag = [&](const int i) -> u32x4 {
       const int ks = i / DB, db = i % DB;
       const uint16_t* vt = vbuf + 16 * ks * D;
@@ -739,8 +762,10 @@ __global__ __launch_bounds__(NW * 64, EXT ? 1 : 2) void fwd_kernel(FwdArgs a) {
       ntw = min(ntw, wave_last / BN + 1);
     }
   }
-  const int t0w = DESC ? nt - ntw : 0;
-  const int t1w = DESC ? nt : ntw;
+  // In iterations: those whose sweep position NG t + gw lies in that range.
+  const int t0w = DESC ? (max(nt - ntw - gw, 0) + NG - 1) / NG : 0;
+  const int t1w = DESC ? (max(nt - gw, 0) + NG - 1) / NG : (max(ntw - gw, 0) + NG - 1) / NG;
+  const bool wact = t1w > t0w;
 
   // Iteration t issues K of tile t+NS (into the buffer K(t) left, whose Sᵀ
   // was formed in iteration t-1) and V of tile t+NS-1 (into the buffer of
@@ -749,11 +774,11 @@ __global__ __launch_bounds__(NW * 64, EXT ? 1 : 2) void fwd_kernel(FwdArgs a) {
   // copies issued in this iteration may still be in flight.
   auto copies = [&](const int t) -> int {
     int n = 0;
-    if (t + NS < nt) {
+    if (t + NS < nti) {
       issue_k(t + NS);
       n += NI;
     }
-    if (t + NS - 1 < nt) {
+    if (t + NS - 1 < nti) {
       issue_v(t + NS - 1);
       n += NI;
     }
@@ -823,7 +848,7 @@ __global__ __launch_bounds__(NW * 64, EXT ? 1 : 2) void fwd_kernel(FwdArgs a) {
   __syncthreads();
 
   f32x16 sa[2], sb[2];
-  if (ntw > 0 && t0w == 0) {
+  if (wact && t0w == 0) {
     qk(0, sa);
     prepare(0, sa);
   }
@@ -837,7 +862,7 @@ __global__ __launch_bounds__(NW * 64, EXT ? 1 : 2) void fwd_kernel(FwdArgs a) {
     // refilled only after the next one.
     for (; t < t0w; ++t) {
       const int n = copies(t);
-      if (ntw > 0 && t + 1 == t0w) {
+      if (wact && t + 1 == t0w) {
         qk(t + 1, sa);
         prepare(t + 1, sa);
       }
@@ -849,7 +874,7 @@ __global__ __launch_bounds__(NW * 64, EXT ? 1 : 2) void fwd_kernel(FwdArgs a) {
   auto keep_of = [&](const int it) __attribute__((always_inline)) -> uint32_t {
     return dropping ? keep_bits(it) : ~0u;
   };
-  if (ntw > 0) {
+  if (wact) {
     for (; t + 2 < t1w; t += 2) {
       full_step(t, sa, sb, keep_of(t));
       full_step(t + 1, sb, sa, keep_of(t + 1));
@@ -863,11 +888,50 @@ __global__ __launch_bounds__(NW * 64, EXT ? 1 : 2) void fwd_kernel(FwdArgs a) {
     t = t1w;
   }
   // Tiles this wave does not need still take part in the copies and barriers.
-  for (; t < nt; ++t) finish(copies(t));
+  for (; t < nti; ++t) finish(copies(t));
+
+  if constexpr (NG == 2) {
+    // Group 1 hands its state (reference maximum, row-sum share and O, per
+    // lane) to the wave of group 0 that owns the same rows, through the K
+    // buffers (O as 16-byte pieces, lane-minor) and the V buffers (maximum
+    // and sum); group 0 rescales both to the larger maximum and adds them.
+    // The last barrier of the sweep came after every read of the tiles.
+    f32x4* xo = (f32x4*)&Ks[0][0] + wi * (DB * 4 * 64) + lane;
+    float* xm = (float*)&Vs[0][0] + wi * 128 + lane;
+    static_assert(NWG * DB * 16 * 64 * 4 <= (int)sizeof(Ks), "O hand-over fits the K buffers");
+    if (gw == 1) {
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4)
+          xo[(db * 4 + q4) * 64] = (f32x4){o[db][4 * q4], o[db][4 * q4 + 1], o[db][4 * q4 + 2], o[db][4 * q4 + 3]};
+      xm[0] = m_ref;
+      xm[64] = l_run;
+    }
+    __syncthreads();
+    if (gw == 0) {
+      const float m1 = xm[0], l1 = xm[64];
+      const float mn = fmaxf(m_ref, m1);
+      if (mn != kNegInf) {
+        const float f0 = m_ref == kNegInf ? 0.f : fast_exp2(m_ref - mn);
+        const float f1 = m1 == kNegInf ? 0.f : fast_exp2(m1 - mn);
+        l_run = l_run * f0 + l1 * f1;
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+          for (int q4 = 0; q4 < 4; ++q4) {
+            const f32x4 x = xo[(db * 4 + q4) * 64];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) o[db][4 * q4 + e] = o[db][4 * q4 + e] * f0 + x[e] * f1;
+          }
+        m_ref = mn;
+      }
+    }
+  }
 
   // Epilogue: out = O / l (0 for a row that saw no key), lse = ln of the sum.
   const float l_tot = sum_halves(l_run);
-  if (qvalid) {
+  if (qvalid && gw == 0) {
     float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
     if (dropping) inv *= a.drop_scale;
     uint16_t* op = a.out + ((size_t)(b * (size_t)a.S_q + qi) * a.H_q + h) * D + 4 * g;

@@ -16,26 +16,36 @@
 namespace sa {
 namespace {
 
+// nw: waves per 32-row slice layout (8: 256-row blocks; 4: 128-row blocks,
+// run by four waves, or by eight in two groups when groups == 2).
 template <class T, int D, bool C, bool M, bool A>
-void launch_fwd(const FwdArgs& args, int nw, hipStream_t st) {
-  if (nw == 8)
+void launch_fwd(const FwdArgs& args, int nw, int groups, hipStream_t st) {
+  if (nw == 8) {
     hipLaunchKernelGGL((fwd_kernel<T, D, C, M, A, 8>), dim3(args.nitems), dim3(512), 0, st, args);
-  else
-    hipLaunchKernelGGL((fwd_kernel<T, D, C, M, A, 4>), dim3(args.nitems), dim3(256), 0, st, args);
+    return;
+  }
+  if constexpr (C && !A) {
+    if (groups == 2) {
+      hipLaunchKernelGGL((fwd_kernel<T, D, C, M, A, 8, false, false, 2>), dim3(args.nitems), dim3(512), 0, st,
+                         args);
+      return;
+    }
+  }
+  hipLaunchKernelGGL((fwd_kernel<T, D, C, M, A, 4>), dim3(args.nitems), dim3(256), 0, st, args);
 }
 
 template <class T, int D>
-void dispatch_fwd(const FwdArgs& args, bool causal, bool mask, bool alibi, int nw, hipStream_t st) {
+void dispatch_fwd(const FwdArgs& args, bool causal, bool mask, bool alibi, int nw, int groups, hipStream_t st) {
   const int key = (causal ? 4 : 0) | (mask ? 2 : 0) | (alibi ? 1 : 0);
   switch (key) {
-    case 0: launch_fwd<T, D, false, false, false>(args, nw, st); break;
-    case 1: launch_fwd<T, D, false, false, true>(args, nw, st); break;
-    case 2: launch_fwd<T, D, false, true, false>(args, nw, st); break;
-    case 3: launch_fwd<T, D, false, true, true>(args, nw, st); break;
-    case 4: launch_fwd<T, D, true, false, false>(args, nw, st); break;
-    case 5: launch_fwd<T, D, true, false, true>(args, nw, st); break;
-    case 6: launch_fwd<T, D, true, true, false>(args, nw, st); break;
-    default: launch_fwd<T, D, true, true, true>(args, nw, st); break;
+    case 0: launch_fwd<T, D, false, false, false>(args, nw, groups, st); break;
+    case 1: launch_fwd<T, D, false, false, true>(args, nw, groups, st); break;
+    case 2: launch_fwd<T, D, false, true, false>(args, nw, groups, st); break;
+    case 3: launch_fwd<T, D, false, true, true>(args, nw, groups, st); break;
+    case 4: launch_fwd<T, D, true, false, false>(args, nw, groups, st); break;
+    case 5: launch_fwd<T, D, true, false, true>(args, nw, groups, st); break;
+    case 6: launch_fwd<T, D, true, true, false>(args, nw, groups, st); break;
+    default: launch_fwd<T, D, true, true, true>(args, nw, groups, st); break;
   }
 }
 
@@ -84,6 +94,7 @@ int sa_attn_fwd(const void* q, const void* k, const void* v, void* out, float* l
   st = num_cus(&cus);
   if (st != SA_OK) return st;
   const int nw = fwd_waves(B, S_q, H_q, causal != 0, cus);
+  const int groups = fwd_groups(nw, causal != 0, alibi_slopes != nullptr);
 
   FwdArgs args;
   args.q = (const uint16_t*)q;
@@ -99,17 +110,17 @@ int sa_attn_fwd(const void* q, const void* k, const void* v, void* out, float* l
   args.alibi2 = 1.0f / std::fabs(scale);
   args.nmb = (S_q + 32 * nw - 1) / (32 * nw);
   args.nitems = B * H_q * args.nmb;
-  args.pair_ncu = fwd_pair_ncu(args.nitems, args.nmb, causal != 0, nw, cus);
+  args.pair_ncu = groups == 1 ? fwd_pair_ncu(args.nitems, args.nmb, causal != 0, nw, cus) : 0;
   args.block_mask = nullptr;
   args.nkb = 0;
   const bool c = causal != 0, m = key_padding_mask != nullptr, al = alibi_slopes != nullptr;
   hipStream_t hs = (hipStream_t)stream;
   if (dtype == SA_F16) {
-    if (D == 64) dispatch_fwd<F16, 64>(args, c, m, al, nw, hs);
-    else dispatch_fwd<F16, 128>(args, c, m, al, nw, hs);
+    if (D == 64) dispatch_fwd<F16, 64>(args, c, m, al, nw, groups, hs);
+    else dispatch_fwd<F16, 128>(args, c, m, al, nw, groups, hs);
   } else {
-    if (D == 64) dispatch_fwd<BF16, 64>(args, c, m, al, nw, hs);
-    else dispatch_fwd<BF16, 128>(args, c, m, al, nw, hs);
+    if (D == 64) dispatch_fwd<BF16, 64>(args, c, m, al, nw, groups, hs);
+    else dispatch_fwd<BF16, 128>(args, c, m, al, nw, groups, hs);
   }
   return launched("attention forward");
 }

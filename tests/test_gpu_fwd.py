@@ -127,6 +127,21 @@ def test_causal_paired_grid_full():
     check(make_inputs(w), what=w.name)
 
 
+@pytest.mark.parametrize("w", [
+    # 192 rows: the second 128-row block sweeps three tiles, so group 1 has
+    # none in the last iteration
+    Workload("groups_odd_tiles", 1, 192, 192, 4, 4, 128, "fp16", causal=True, seed=141),
+    # 100 queries at the end of 1000 keys: 16 tiles, rows skip the last one
+    Workload("groups_bottom_right", 2, 100, 1000, 4, 2, 64, "bf16", causal=True, random_tail=300, seed=142),
+    # one tile in all (group 1 idle throughout)
+    Workload("groups_one_tile", 1, 40, 40, 2, 2, 128, "bf16", causal=True, seed=143),
+], ids=lambda w: w.name)
+def test_two_group_causal(w):
+    """Causal shapes that take the two-group forward (eight waves over
+    128-row blocks, odd and even tile positions), checked in full."""
+    check(make_inputs(w), what=w.name)
+
+
 def test_config5_sampled():
     w = WORKLOADS["c5_alibi_8192"]
     inp = make_inputs(w)
