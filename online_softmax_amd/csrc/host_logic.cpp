@@ -186,11 +186,13 @@ int fwd_waves(int B, int S_q, int H_q, bool causal, int num_cu) {
   return wg8 >= need ? 8 : 4;
 }
 
-int fwd_groups(int nw, bool causal, bool alibi) {
-  // Measured against the paired four-wave grids (same-process A/B): c3 causal
-  // 90.2 -> 86.9 us, [2,1024,8,64] causal with padding 18.7 -> 17.0 us; with
-  // ALiBi the c3-shaped causal forward was slower (91.5 -> 97.7 us).
-  return nw == 4 && causal && !alibi ? 2 : 1;
+int fwd_groups(int nw, bool causal) {
+  // Measured against four-wave grids with a heavy and a light block paired
+  // on each CU (same-process A/B): [1,4096,16,128] causal 89.7-90.2 ->
+  // 86.9-88.2 us, [2,1024,8,64] causal with padding 18.7-19.1 -> 17.0-17.3
+  // us, with ALiBi (descending sweep) 19.7 -> 18.5 us, and [1,8192,8,128]
+  // causal ALiBi with padding 169-174 -> 154-160 us.
+  return nw == 4 && causal ? 2 : 1;
 }
 
 int fwd_pair_ncu(int nitems, int nmb, bool causal, int nw, int num_cu) {

@@ -97,15 +97,15 @@ int decode_fused_num_splits(int B, int S_k, int H_q, int H_kv, int num_cu);
 // they are used when there are enough of them to keep every CU busy (for
 // causal work, enough to balance the unequal blocks).
 int fwd_waves(int B, int S_q, int H_q, bool causal, int num_cu);
-// The paired causal block mapping of the dense forward and of the backward's
-// dq kernel (pair_ncu): num_cu when a causal grid of four-wave workgroups
+// The paired causal block mapping of the backward's dq kernel (pair_ncu):
+// num_cu when a causal grid of four-wave workgroups
 // (two resident per CU) has exactly two workgroups per CU and an even number
 // of blocks per head, else 0.
 int fwd_pair_ncu(int nitems, int nmb, bool causal, int nw, int num_cu);
 // Wave groups of the forward kernel: 2 (eight waves in two groups over
-// 128-row blocks, heaviest blocks first) where the causal forward without
-// ALiBi would otherwise run four-wave workgroups, else 1.
-int fwd_groups(int nw, bool causal, bool alibi);
+// 128-row blocks, heaviest blocks first) where the causal forward would
+// otherwise run four-wave workgroups, else 1.
+int fwd_groups(int nw, bool causal);
 // Keys per split for a split count (a multiple of kDecodeStepKeys).
 int decode_chunk(int S_k, int splits);
 size_t decode_workspace_size(int B, int H_q, int S_k, int D);

@@ -78,9 +78,6 @@ struct FwdArgs {
   float alibi2;  // log2(e) / |scale log2(e)| = 1 / |scale|: bias to accumulator units
   int nmb;       // query blocks per (batch, head)
   int nitems;    // B * H_q * nmb
-  // Causal sweeps whose whole grid is resident at two workgroups per CU:
-  // the number of CUs (workgroups j and j + pair_ncu then share a CU), else 0.
-  int pair_ncu;
   const uint8_t* block_mask;  // block-sparse mode: [B, H_q, nmb, nkb], nonzero = visit
   int nkb;                    // key blocks of kSparseBlock per row of block_mask
   // Extended mode.  Bias element (b, h, i, j) at bias[b sb + h sh + i sq + j]
@@ -198,26 +195,11 @@ __global__ __launch_bounds__(NW * 64, EXT ? 1 : 2) void fwd_kernel(FwdArgs a) {
   const int gw = NG == 1 ? 0 : w / NWG;  // this wave's group
   const int wi = w - gw * NWG;           // and its place in the group
 
-  int bh, mb;
-  if (CAUSAL && !SPARSE && a.pair_ncu > 0) {
-    // The whole grid is resident, two workgroups per CU, and the hardware
-    // places workgroups j and j + pair_ncu on one CU: they take blocks
-    // nmb - 1 - l and l of one head, so that every CU carries the same
-    // causal work (nmb + 1 blocks' worth); consecutive j go to different
-    // XCDs and heads repeat every B * H_q, so each XCD keeps to a few heads.
-    const int ncu = a.pair_ncu, j = blockIdx.x;
-    const int p = j < ncu ? j : j - ncu;
-    const int nbh = a.nitems / a.nmb;
-    bh = p % nbh;
-    const int lvl = p / nbh;
-    mb = j < ncu ? a.nmb - 1 - lvl : lvl;
-  } else {
-    const int item = xcd_contiguous(blockIdx.x, a.nitems);
-    bh = item / a.nmb;
-    const int mbi = item - bh * a.nmb;
-    // Causal blocks are issued heaviest (last rows) first.
-    mb = CAUSAL ? a.nmb - 1 - mbi : mbi;
-  }
+  const int item = xcd_contiguous(blockIdx.x, a.nitems);
+  const int bh = item / a.nmb;
+  const int mbi = item - bh * a.nmb;
+  // Causal blocks are issued heaviest (last rows) first.
+  const int mb = CAUSAL ? a.nmb - 1 - mbi : mbi;
   const int b = bh / a.H_q, h = bh - b * a.H_q, hk = h / a.G;
   const int m0 = mb * BM;
   const int off = a.S_k - a.S_q;  // bottom-right alignment of the causal rule
@@ -344,11 +326,15 @@ __global__ __launch_bounds__(NW * 64, EXT ? 1 : 2) void fwd_kernel(FwdArgs a) {
   // tile, where the largest biases sit, so the running maximum rarely needs
   // raising afterwards (in key order it would rise on nearly every tile for
   // the steeper slopes); and the workgroups of one head still walk the shared
-  // tiles from key 0 together, which keeps them in L2.  Otherwise the order
-  // is plain 0 .. nt-1.
+  // tiles from key 0 together, which keeps them in L2.  In the two-group mode
+  // the whole sweep runs from the last tile down: the groups take alternate
+  // positions, so with the band first the rows of group 0 whose diagonal is
+  // the band's second tile would start on key 0.  Otherwise the order is
+  // plain 0 .. nt-1.
   const int nb = BAND ? min(nt, BM / BN) : 0;
   auto tile_of = [&](int it) -> int {
     if constexpr (SPARSE) return __builtin_amdgcn_readfirstlane((int)Tl[DESC ? nt - 1 - it : it]);
+    else if constexpr (NG == 2 && BAND) return nt - 1 - it;
     else return it < nb ? nt - 1 - it : it - nb;
   };
   // Iteration t stages the tiles of sweep positions NG t .. NG t + NG - 1

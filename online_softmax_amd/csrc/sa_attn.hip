@@ -24,7 +24,7 @@ void launch_fwd(const FwdArgs& args, int nw, int groups, hipStream_t st) {
     hipLaunchKernelGGL((fwd_kernel<T, D, C, M, A, 8>), dim3(args.nitems), dim3(512), 0, st, args);
     return;
   }
-  if constexpr (C && !A) {
+  if constexpr (C) {
     if (groups == 2) {
       hipLaunchKernelGGL((fwd_kernel<T, D, C, M, A, 8, false, false, 2>), dim3(args.nitems), dim3(512), 0, st,
                          args);
@@ -94,7 +94,7 @@ int sa_attn_fwd(const void* q, const void* k, const void* v, void* out, float* l
   st = num_cus(&cus);
   if (st != SA_OK) return st;
   const int nw = fwd_waves(B, S_q, H_q, causal != 0, cus);
-  const int groups = fwd_groups(nw, causal != 0, alibi_slopes != nullptr);
+  const int groups = fwd_groups(nw, causal != 0);
 
   FwdArgs args;
   args.q = (const uint16_t*)q;
@@ -110,7 +110,6 @@ int sa_attn_fwd(const void* q, const void* k, const void* v, void* out, float* l
   args.alibi2 = 1.0f / std::fabs(scale);
   args.nmb = (S_q + 32 * nw - 1) / (32 * nw);
   args.nitems = B * H_q * args.nmb;
-  args.pair_ncu = groups == 1 ? fwd_pair_ncu(args.nitems, args.nmb, causal != 0, nw, cus) : 0;
   args.block_mask = nullptr;
   args.nkb = 0;
   const bool c = causal != 0, m = key_padding_mask != nullptr, al = alibi_slopes != nullptr;

@@ -71,7 +71,6 @@ int sa_attn_fwd_ext(const void* q, const void* k, const void* v, void* out, floa
   args.alibi2 = 1.0f / std::fabs(scale);
   args.nmb = (S_q + 127) / 128;
   args.nitems = B * H_q * args.nmb;
-  args.pair_ncu = 0;
   args.block_mask = nullptr;
   args.nkb = 0;
   args.bias = attn_bias;

@@ -69,7 +69,6 @@ int sa_attn_fwd_block_sparse(const void* q, const void* k, const void* v, void* 
   args.alibi2 = 1.0f / std::fabs(scale);
   args.nmb = (S_q + kSparseBlock - 1) / kSparseBlock;
   args.nitems = B * H_q * args.nmb;
-  args.pair_ncu = 0;
   args.block_mask = block_mask;
   args.nkb = (S_k + kSparseBlock - 1) / kSparseBlock;
   const bool c = causal != 0, m = key_padding_mask != nullptr, al = alibi_slopes != nullptr;

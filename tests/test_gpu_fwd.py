@@ -105,9 +105,9 @@ def test_config3_sampled(name):
 
 
 def test_causal_grid_every_row_written():
-    """c3 causal at full size (one resident grid of 512 four-wave workgroups
-    on a 256-CU device, where the paired block mapping applies): every row of
-    out and lse is written, starting from NaN."""
+    """c3 causal at full size (512 eight-wave workgroups in two groups over
+    128-row blocks, issued heaviest first): every row of out and lse is
+    written, starting from NaN."""
     w = WORKLOADS["c3_causal_4096"]
     q, k, v, _, _ = to_dev(make_inputs(w))
     out = torch.full_like(q, float("nan"))
@@ -117,13 +117,13 @@ def test_causal_grid_every_row_written():
     assert torch.isfinite(out).all() and torch.isfinite(lse).all()
 
 
-def test_causal_paired_grid_full():
-    """A causal grid of exactly two four-wave workgroups per CU on a 256-CU
-    device (B * H_q * 4 blocks = 512), checked in full."""
+def test_causal_grid_two_rounds_full():
+    """A causal grid of 512 128-row blocks (B * H_q * 4), two per CU on a
+    256-CU device, so that the heaviest-first order has a second round to
+    fill; checked in full."""
     ncu = torch.cuda.get_device_properties(0).multi_processor_count
-    w = Workload("paired_grid", 2, 512, 512, 64, 8, 64, "fp16", causal=True, seed=131)
-    print(f"[fwd] paired mapping {'applies' if 2 * 64 * 4 == 2 * ncu else 'does not apply'} ({ncu} CUs)",
-          flush=True)
+    w = Workload("two_round_grid", 2, 512, 512, 64, 8, 64, "fp16", causal=True, seed=131)
+    print(f"[fwd] {2 * 64 * 4} blocks on {ncu} CUs", flush=True)
     check(make_inputs(w), what=w.name)
 
 
@@ -135,10 +135,14 @@ def test_causal_paired_grid_full():
     Workload("groups_bottom_right", 2, 100, 1000, 4, 2, 64, "bf16", causal=True, random_tail=300, seed=142),
     # one tile in all (group 1 idle throughout)
     Workload("groups_one_tile", 1, 40, 40, 2, 2, 128, "bf16", causal=True, seed=143),
+    Workload("groups_alibi_odd", 1, 192, 192, 4, 4, 128, "bf16", causal=True, alibi=True, random_tail=50,
+             seed=144),
+    Workload("groups_alibi_bottom_right", 1, 70, 600, 4, 2, 64, "fp16", causal=True, alibi=True, seed=145),
 ], ids=lambda w: w.name)
 def test_two_group_causal(w):
     """Causal shapes that take the two-group forward (eight waves over
-    128-row blocks, odd and even tile positions), checked in full."""
+    128-row blocks, odd and even tile positions), checked in full; the
+    ALiBi cases sweep from the last tile down."""
     check(make_inputs(w), what=w.name)
 
 
