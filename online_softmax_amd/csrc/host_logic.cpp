@@ -186,15 +186,6 @@ int fwd_waves(int B, int S_q, int H_q, bool causal, int num_cu) {
   return wg8 >= need ? 8 : 4;
 }
 
-int fwd_groups(int nw, bool causal) {
-  // Measured against four-wave grids with a heavy and a light block paired
-  // on each CU (same-process A/B): [1,4096,16,128] causal 89.7-90.2 ->
-  // 86.9-88.2 us, [2,1024,8,64] causal with padding 18.7-19.1 -> 17.0-17.3
-  // us, with ALiBi (descending sweep) 19.7 -> 18.5 us, and [1,8192,8,128]
-  // causal ALiBi with padding 169-174 -> 154-160 us.
-  return nw == 4 && causal ? 2 : 1;
-}
-
 int fwd_pair_ncu(int nitems, int nmb, bool causal, int nw, int num_cu) {
   if (!causal || nw != 4 || num_cu <= 0 || nmb <= 0 || nmb % 2) return 0;
   return (int64_t)nitems == 2 * (int64_t)num_cu ? num_cu : 0;

@@ -102,10 +102,6 @@ int fwd_waves(int B, int S_q, int H_q, bool causal, int num_cu);
 // (two resident per CU) has exactly two workgroups per CU and an even number
 // of blocks per head, else 0.
 int fwd_pair_ncu(int nitems, int nmb, bool causal, int nw, int num_cu);
-// Wave groups of the forward kernel: 2 (eight waves in two groups over
-// 128-row blocks, heaviest blocks first) where the causal forward would
-// otherwise run four-wave workgroups, else 1.
-int fwd_groups(int nw, bool causal);
 // Keys per split for a split count (a multiple of kDecodeStepKeys).
 int decode_chunk(int S_k, int splits);
 size_t decode_workspace_size(int B, int H_q, int S_k, int D);

@@ -16,36 +16,35 @@
 namespace sa {
 namespace {
 
-// nw: waves per 32-row slice layout (8: 256-row blocks; 4: 128-row blocks,
-// run by four waves, or by eight in two groups when groups == 2).
+// nw = 8: 256-row blocks of eight waves.  nw = 4: 128-row blocks, run by
+// four waves, or under the causal rule by eight waves in two groups.  The
+// two-group kernel replaced four-wave grids with a heavy and a light causal
+// block paired on each CU; same-process A/B: [1,4096,16,128] causal
+// 89.7-90.2 -> 86.9-88.2 us, [2,1024,8,64] causal with padding 18.7-19.1 ->
+// 17.0-17.3 us (with ALiBi 19.7 -> 18.5 us), [1,8192,8,128] causal ALiBi with
+// padding 169-174 -> 154-160 us.
 template <class T, int D, bool C, bool M, bool A>
-void launch_fwd(const FwdArgs& args, int nw, int groups, hipStream_t st) {
-  if (nw == 8) {
+void launch_fwd(const FwdArgs& args, int nw, hipStream_t st) {
+  if (nw == 8)
     hipLaunchKernelGGL((fwd_kernel<T, D, C, M, A, 8>), dim3(args.nitems), dim3(512), 0, st, args);
-    return;
-  }
-  if constexpr (C) {
-    if (groups == 2) {
-      hipLaunchKernelGGL((fwd_kernel<T, D, C, M, A, 8, false, false, 2>), dim3(args.nitems), dim3(512), 0, st,
-                         args);
-      return;
-    }
-  }
-  hipLaunchKernelGGL((fwd_kernel<T, D, C, M, A, 4>), dim3(args.nitems), dim3(256), 0, st, args);
+  else if constexpr (C)
+    hipLaunchKernelGGL((fwd_kernel<T, D, C, M, A, 8, false, false, 2>), dim3(args.nitems), dim3(512), 0, st, args);
+  else
+    hipLaunchKernelGGL((fwd_kernel<T, D, C, M, A, 4>), dim3(args.nitems), dim3(256), 0, st, args);
 }
 
 template <class T, int D>
-void dispatch_fwd(const FwdArgs& args, bool causal, bool mask, bool alibi, int nw, int groups, hipStream_t st) {
+void dispatch_fwd(const FwdArgs& args, bool causal, bool mask, bool alibi, int nw, hipStream_t st) {
   const int key = (causal ? 4 : 0) | (mask ? 2 : 0) | (alibi ? 1 : 0);
   switch (key) {
-    case 0: launch_fwd<T, D, false, false, false>(args, nw, groups, st); break;
-    case 1: launch_fwd<T, D, false, false, true>(args, nw, groups, st); break;
-    case 2: launch_fwd<T, D, false, true, false>(args, nw, groups, st); break;
-    case 3: launch_fwd<T, D, false, true, true>(args, nw, groups, st); break;
-    case 4: launch_fwd<T, D, true, false, false>(args, nw, groups, st); break;
-    case 5: launch_fwd<T, D, true, false, true>(args, nw, groups, st); break;
-    case 6: launch_fwd<T, D, true, true, false>(args, nw, groups, st); break;
-    default: launch_fwd<T, D, true, true, true>(args, nw, groups, st); break;
+    case 0: launch_fwd<T, D, false, false, false>(args, nw, st); break;
+    case 1: launch_fwd<T, D, false, false, true>(args, nw, st); break;
+    case 2: launch_fwd<T, D, false, true, false>(args, nw, st); break;
+    case 3: launch_fwd<T, D, false, true, true>(args, nw, st); break;
+    case 4: launch_fwd<T, D, true, false, false>(args, nw, st); break;
+    case 5: launch_fwd<T, D, true, false, true>(args, nw, st); break;
+    case 6: launch_fwd<T, D, true, true, false>(args, nw, st); break;
+    default: launch_fwd<T, D, true, true, true>(args, nw, st); break;
   }
 }
 
@@ -94,7 +93,6 @@ int sa_attn_fwd(const void* q, const void* k, const void* v, void* out, float* l
   st = num_cus(&cus);
   if (st != SA_OK) return st;
   const int nw = fwd_waves(B, S_q, H_q, causal != 0, cus);
-  const int groups = fwd_groups(nw, causal != 0);
 
   FwdArgs args;
   args.q = (const uint16_t*)q;
@@ -115,11 +113,11 @@ int sa_attn_fwd(const void* q, const void* k, const void* v, void* out, float* l
   const bool c = causal != 0, m = key_padding_mask != nullptr, al = alibi_slopes != nullptr;
   hipStream_t hs = (hipStream_t)stream;
   if (dtype == SA_F16) {
-    if (D == 64) dispatch_fwd<F16, 64>(args, c, m, al, nw, groups, hs);
-    else dispatch_fwd<F16, 128>(args, c, m, al, nw, groups, hs);
+    if (D == 64) dispatch_fwd<F16, 64>(args, c, m, al, nw, hs);
+    else dispatch_fwd<F16, 128>(args, c, m, al, nw, hs);
   } else {
-    if (D == 64) dispatch_fwd<BF16, 64>(args, c, m, al, nw, groups, hs);
-    else dispatch_fwd<BF16, 128>(args, c, m, al, nw, groups, hs);
+    if (D == 64) dispatch_fwd<BF16, 64>(args, c, m, al, nw, hs);
+    else dispatch_fwd<BF16, 128>(args, c, m, al, nw, hs);
   }
   return launched("attention forward");
 }
