@@ -453,7 +453,7 @@ def main():
                              f"H_kv={p.w.H_kv} D={p.w.D} {p.w.dtype} causal={p.w.causal} "
                              f"mask={'tails ' + str(p.tails) if p.tails else 'none'} "
                              f"alibi={p.w.alibi}" for p in parts],
-                   "wall_s_lead_plus_timed": round(wall, 4),
+                   "wall_s_lead_warmup_timed": round(wall, 4),
                    "device_lead_ms": round(n_lead * mm_ms, 3)},
     }
     prefill = [(p, t) for p, t in zip(parts, part_ms) if not p.w.decode and not p.bwd]
