@@ -75,7 +75,10 @@ typedef struct ihipStream_t* sa_stream_t;
  *   scale  multiplies q.k in float32 (callers usually pass 1/sqrt(D))
  *   causal 0 or 1 (bottom-right aligned, see above)
  *   key_padding_mask [B, S_k] uint8 device, nonzero = keep; NULL = all keep
- *   alibi_slopes     [H_q] float32 device; NULL = no bias
+ *   alibi_slopes     [H_q] float32 device; NULL = no bias.  The kernels add
+ *                    a bias in units of 1 / |scale|, so with slopes the scale
+ *                    must be nonzero with 1 / |scale| finite in float32
+ *                    (SA_ERR_INVALID_ARG otherwise)
  *
  * B == 0 or S_q == 0 is a successful no-op.  S_k == 0 writes out = 0 and
  * lse = -inf.  Errors: SA_ERR_INVALID_ARG, SA_ERR_UNSUPPORTED, SA_ERR_HIP.
@@ -124,6 +127,8 @@ int sa_attn_fwd_block_sparse(const void* q, const void* k, const void* v, void* 
  *              the ALiBi bias; -inf hides the key.  Strides are in elements,
  *              non-negative multiples of 4 (0 broadcasts that axis); the
  *              pointer is 16-byte aligned.  Entries must not be +inf or NaN.
+ *              As for alibi_slopes, a bias needs a nonzero scale with
+ *              1 / |scale| finite (SA_ERR_INVALID_ARG otherwise).
  *   dropout_p  in [0, 1); 0 turns dropout off.  A probability P[i, j] of
  *              (batch b, query head h) is kept when word (j mod 4) of
  *              Philox4x32-10 (Salmon et al., SC'11) with counter
@@ -175,7 +180,8 @@ size_t sa_attn_decode_workspace_size(int B, int H_q, int S_k, int D);
  *     sa_attn_decode_workspace_size(B, H_q, S_k, D) bytes, 16-byte aligned;
  *     its contents on entry do not matter and on return are unspecified.
  *     Calls that may run at the same time must not share a workspace.
- *   The scale must be nonzero when alibi_slopes is given.
+ *   The scale must be nonzero, with 1 / |scale| finite, when alibi_slopes
+ *   is given.
  *
  * B == 0 is a no-op; S_k == 0 writes out = 0, lse = -inf.  Errors:
  * SA_ERR_INVALID_ARG (also when one split would span 4 GiB or more of

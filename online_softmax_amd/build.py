@@ -55,24 +55,22 @@ def _run(cmd, verbose):
 def build(verbose: bool = False) -> Path:
     hipcc = _hipcc()
     BUILD.mkdir(exist_ok=True)
+    for p in BUILD.glob("*.o"):
+        p.unlink()
     host_o = BUILD / "host_logic.o"
-    dev_o = BUILD / "sa_attn.o"
-    bwd_o = BUILD / "sa_attn_bwd.o"
-    sparse_o = BUILD / "sa_attn_sparse.o"
-    ext_o = BUILD / "sa_attn_ext.o"
-    for p in (host_o, dev_o, bwd_o, sparse_o, ext_o):
-        if p.exists():
-            p.unlink()
-    steps = [["g++", "-O2", "-std=c++17", "-fPIC", "-Wall", "-c", CSRC / "host_logic.cpp", "-o", host_o],
-             [hipcc, *HIP_FLAGS, "-c", CSRC / "sa_attn.hip", "-o", dev_o],
-             [hipcc, *HIP_FLAGS, *BWD_FLAGS, "-c", CSRC / "sa_attn_bwd.hip", "-o", bwd_o],
-             [hipcc, *HIP_FLAGS, "-c", CSRC / "sa_attn_sparse.hip", "-o", sparse_o],
-             [hipcc, *HIP_FLAGS, "-c", CSRC / "sa_attn_ext.hip", "-o", ext_o]]
+    steps = [["g++", "-O2", "-std=c++17", "-fPIC", "-Wall", "-c", CSRC / "host_logic.cpp", "-o", host_o]]
+    objs = []
+    # One compilation unit per entry-point file, built in parallel.
+    for src in sorted(CSRC.glob("*.hip")):
+        obj = BUILD / (src.stem + ".o")
+        extra = BWD_FLAGS if src.stem == "sa_attn_bwd" else []
+        steps.append([hipcc, *HIP_FLAGS, *extra, "-c", src, "-o", obj])
+        objs.append(obj)
     with ThreadPoolExecutor(len(steps)) as pool:
         for f in [pool.submit(_run, cmd, verbose) for cmd in steps]:
             f.result()
     tmp = LIB.with_suffix(".so.tmp")
-    _run([hipcc, "-shared", f"--offload-arch={ARCH}", "-o", tmp, dev_o, bwd_o, sparse_o, ext_o, host_o], verbose)
+    _run([hipcc, "-shared", f"--offload-arch={ARCH}", "-o", tmp, *objs, host_o], verbose)
     os.replace(tmp, LIB)
     return LIB
 

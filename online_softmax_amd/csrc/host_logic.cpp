@@ -76,8 +76,9 @@ int check_fwd(const FwdShape& s, bool* noop) {
   if (st != SA_OK) return st;
   if (s.S_q < 0) return fail(SA_ERR_INVALID_ARG, "negative S_q=%d", s.S_q);
   if (s.causal != 0 && s.causal != 1) return fail(SA_ERR_INVALID_ARG, "causal must be 0 or 1");
-  if (s.slopes && s.scale == 0.f)
-    return fail(SA_ERR_INVALID_ARG, "scale must be nonzero when ALiBi slopes are given");
+  // The kernels add a bias in units of 1 / |scale|, which must be finite.
+  if (s.slopes && !std::isfinite(1.0f / std::fabs(s.scale)))
+    return fail(SA_ERR_INVALID_ARG, "scale must be nonzero (1/|scale| finite) when ALiBi slopes are given");
   if (s.B == 0 || s.S_q == 0) { *noop = true; return SA_OK; }
   int64_t nq = 1, nk = 1;
   if (!mul_ok(&nq, s.B) || !mul_ok(&nq, s.S_q) || !mul_ok(&nq, s.H_q) || !mul_ok(&nq, s.D) ||
@@ -134,6 +135,8 @@ uint32_t drop_threshold(double p) {
 int check_ext(const FwdShape& s, const ExtShape& e, bool* noop) {
   if (!(e.dropout_p >= 0.0 && e.dropout_p < 1.0))
     return fail(SA_ERR_INVALID_ARG, "dropout_p must be in [0, 1) (got %g)", e.dropout_p);
+  if (e.bias && !std::isfinite(1.0f / std::fabs(s.scale)))
+    return fail(SA_ERR_INVALID_ARG, "scale must be nonzero (1/|scale| finite) when attn_bias is given");
   int st = check_fwd(s, noop);
   if (st != SA_OK || *noop || !e.bias || s.S_k == 0) return st;
   if (e.sb < 0 || e.sh < 0 || e.sq < 0 || e.sb % 4 || e.sh % 4 || e.sq % 4)
@@ -264,6 +267,13 @@ int check_decode_fused(const DecodeShape& s, bool* noop) {
 
 int check_decode(const DecodeShape& s, bool* noop) {
   *noop = false;
+  if (s.B > 0 && s.H_q > 0 && s.S_k >= 0 && s.D > 0 && decode_workspace_size(s.B, s.H_q, s.S_k, s.D) == 0)
+    return fail(SA_ERR_INVALID_ARG, "tensor sizes overflow");
+  return check_decode_need(s, decode_workspace_size(s.B, s.H_q, s.S_k, s.D), noop);
+}
+
+int check_decode_need(const DecodeShape& s, size_t need, bool* noop) {
+  *noop = false;
   int st = check_common(s.dtype, s.D, s.B, s.S_k, s.H_q, s.H_kv, s.scale);
   if (st != SA_OK) return st;
   if (s.B == 0) { *noop = true; return SA_OK; }
@@ -271,19 +281,21 @@ int check_decode(const DecodeShape& s, bool* noop) {
   if (!mul_ok(&nk, s.B) || !mul_ok(&nk, s.S_k) || !mul_ok(&nk, s.H_kv) || !mul_ok(&nk, s.D))
     return fail(SA_ERR_INVALID_ARG, "tensor sizes overflow");
   if (!s.q || !s.out) return fail(SA_ERR_INVALID_ARG, "q and out must not be NULL");
-  if (s.slopes && s.scale == 0.f)
-    return fail(SA_ERR_INVALID_ARG, "scale must be nonzero when ALiBi slopes are given");
+  // The kernels add a bias in units of 1 / |scale|, which must be finite.
+  if (s.slopes && !std::isfinite(1.0f / std::fabs(s.scale)))
+    return fail(SA_ERR_INVALID_ARG, "scale must be nonzero (1/|scale| finite) when ALiBi slopes are given");
   if (s.S_k > 0 && (!s.k || !s.v)) return fail(SA_ERR_INVALID_ARG, "k_cache and v_cache must not be NULL when S_k > 0");
   if (!aligned(s.q, 16) || !aligned(s.out, 16) || (s.k && !aligned(s.k, 16)) || (s.v && !aligned(s.v, 16)))
     return fail(SA_ERR_INVALID_ARG, "q, k_cache, v_cache and out must be 16-byte aligned");
   if (s.lse && !aligned(s.lse, 4)) return fail(SA_ERR_INVALID_ARG, "lse must be 4-byte aligned");
   if (s.slopes && !aligned(s.slopes, 4)) return fail(SA_ERR_INVALID_ARG, "alibi_slopes must be 4-byte aligned");
-  const size_t need = decode_workspace_size(s.B, s.H_q, s.S_k, s.D);
-  if (need == 0) return fail(SA_ERR_INVALID_ARG, "tensor sizes overflow");
-  if (!s.workspace) return fail(SA_ERR_WORKSPACE, "workspace is NULL (%zu bytes needed)", need);
-  if (!aligned(s.workspace, 16)) return fail(SA_ERR_WORKSPACE, "workspace must be 16-byte aligned");
-  if (s.workspace_bytes < need)
-    return fail(SA_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed", s.workspace_bytes, need);
+  // need == 0: the argument checks only (no workspace given yet).
+  if (need > 0) {
+    if (!s.workspace) return fail(SA_ERR_WORKSPACE, "workspace is NULL (%zu bytes needed)", need);
+    if (!aligned(s.workspace, 16)) return fail(SA_ERR_WORKSPACE, "workspace must be 16-byte aligned");
+    if (s.workspace_bytes < need)
+      return fail(SA_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed", s.workspace_bytes, need);
+  }
   const size_t qb = (size_t)s.B * s.H_q * s.D * 2, kb = (size_t)nk * 2;
   const size_t lb = (size_t)s.B * s.H_q * 4;
   const void* ins[5] = {s.q, s.k, s.v, s.mask, s.slopes};
@@ -312,8 +324,9 @@ int check_bwd(const BwdShape& s, bool* noop) {
   if (st != SA_OK) return st;
   if (s.S_q < 0) return fail(SA_ERR_INVALID_ARG, "negative S_q=%d", s.S_q);
   if (s.causal != 0 && s.causal != 1) return fail(SA_ERR_INVALID_ARG, "causal must be 0 or 1");
-  if (s.slopes && s.scale == 0.f)
-    return fail(SA_ERR_INVALID_ARG, "scale must be nonzero when ALiBi slopes are given");
+  // The kernels add a bias in units of 1 / |scale|, which must be finite.
+  if (s.slopes && !std::isfinite(1.0f / std::fabs(s.scale)))
+    return fail(SA_ERR_INVALID_ARG, "scale must be nonzero (1/|scale| finite) when ALiBi slopes are given");
   // With no query rows dk and dv are zero; with no keys dq is zero: both are
   // still written.  Only an empty batch, or no rows and no keys, is a no-op.
   if (s.B == 0 || (s.S_q == 0 && s.S_k == 0)) { *noop = true; return SA_OK; }

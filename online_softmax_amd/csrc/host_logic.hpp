@@ -59,6 +59,9 @@ const char* status_string(int status);
 // when the call is valid but has nothing to compute.
 int check_fwd(const FwdShape& s, bool* noop);
 int check_decode(const DecodeShape& s, bool* noop);
+// check_decode with the workspace held to `need` bytes instead of
+// decode_workspace_size (need == 0: the arguments only, no workspace).
+int check_decode_need(const DecodeShape& s, size_t need, bool* noop);
 // The single-kernel decode: its workspace starts with kDecodeArriveBytes of
 // 32-bit arrival counters, one per head group (so at most kDecodeMaxGroups
 // groups), zero before the first call; the partial area follows at that

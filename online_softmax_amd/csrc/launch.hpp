@@ -4,6 +4,7 @@
 
 #include <mutex>
 
+#include "../../include/sa_attn.h"
 #include "host_logic.hpp"
 
 namespace sa {
@@ -34,5 +35,10 @@ inline int num_cus(int* out) {
   *out = cus[dev];
   return SA_OK;
 }
+
+// Split and merge launches of a validated decode (sa_attn.hip) over `splits`
+// splits with its partial results in `workspace`, which holds at least
+// decode_layout(B, H_q, splits, D).bytes.
+int launch_decode(const DecodeShape& s, int splits, void* workspace, sa_stream_t stream);
 
 }  // namespace sa

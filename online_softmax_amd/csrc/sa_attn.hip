@@ -73,6 +73,55 @@ void dispatch_decode_fused(const DecArgs& args, int nwg, bool mask, bool alibi, 
 }
 
 }  // namespace
+
+// Split and merge launches of a validated decode over `splits` splits, with
+// its partial results in `workspace` (decode_layout(B, H_q, splits, D)).
+int launch_decode(const DecodeShape& s, int splits, void* workspace, sa_stream_t stream) {
+  const int G = s.H_q / s.H_kv;
+  const int n_hg = (G + kDecodeHeadGroup - 1) / kDecodeHeadGroup;
+  const int chunk = decode_chunk(s.S_k, splits);
+  const int64_t nwg = (int64_t)s.B * s.H_kv * n_hg * splits;
+  if (nwg > INT32_MAX || (int64_t)s.B * s.H_q * (s.D / 16) > INT32_MAX)
+    return fail(SA_ERR_INVALID_ARG, "too many decode workgroups");
+  if (!decode_offsets_fit(chunk, s.H_kv, s.D))
+    return fail(SA_ERR_INVALID_ARG, "one decode split would span 4 GiB or more of k_cache");
+
+  const DecodeLayout lay = decode_layout(s.B, s.H_q, splits, s.D);
+  DecArgs args;
+  args.q = (const uint16_t*)s.q;
+  args.k = (const uint16_t*)s.k;
+  args.v = (const uint16_t*)s.v;
+  args.mask = s.mask;
+  args.slopes = s.slopes;
+  args.out = (uint16_t*)s.out;
+  args.lse = const_cast<float*>(s.lse);
+  args.ws_o = (float*)((char*)workspace + lay.o_offset);
+  args.ws_lse = (float*)((char*)workspace + lay.lse_offset);
+  args.B = s.B; args.S_k = s.S_k; args.H_q = s.H_q; args.H_kv = s.H_kv; args.G = G;
+  args.n_hg = n_hg; args.splits = splits; args.chunk = chunk;
+  args.scale2 = s.scale * kLog2e;
+  args.alibi2 = s.scale != 0.f ? 1.0f / std::fabs(s.scale) : 0.f;
+  args.arrive = nullptr;
+
+  MergeArgs margs;
+  margs.ws_o = args.ws_o;
+  margs.ws_lse = args.ws_lse;
+  margs.out = (uint16_t*)s.out;
+  margs.lse = const_cast<float*>(s.lse);
+  margs.splits = splits;
+
+  const bool m = s.mask != nullptr, al = s.slopes != nullptr;
+  hipStream_t hs = (hipStream_t)stream;
+  if (s.dtype == SA_F16) {
+    if (s.D == 64) dispatch_decode<F16, 64>(args, margs, (int)nwg, m, al, hs);
+    else dispatch_decode<F16, 128>(args, margs, (int)nwg, m, al, hs);
+  } else {
+    if (s.D == 64) dispatch_decode<BF16, 64>(args, margs, (int)nwg, m, al, hs);
+    else dispatch_decode<BF16, 128>(args, margs, (int)nwg, m, al, hs);
+  }
+  return launched("decode");
+}
+
 }  // namespace sa
 
 extern "C" {
@@ -148,51 +197,7 @@ int sa_attn_decode(const void* q, const void* k_cache, const void* v_cache, void
   int cus = 0;
   st = num_cus(&cus);
   if (st != SA_OK) return st;
-
-  const int G = H_q / H_kv;
-  const int n_hg = (G + kDecodeHeadGroup - 1) / kDecodeHeadGroup;
-  const int splits = decode_num_splits(B, S_k, H_q, H_kv, cus);
-  const int chunk = decode_chunk(S_k, splits);
-  const int64_t nwg = (int64_t)B * H_kv * n_hg * splits;
-  if (nwg > INT32_MAX || (int64_t)B * H_q * (D / 16) > INT32_MAX)
-    return fail(SA_ERR_INVALID_ARG, "too many decode workgroups");
-  if (!decode_offsets_fit(chunk, H_kv, D))
-    return fail(SA_ERR_INVALID_ARG, "one decode split would span 4 GiB or more of k_cache");
-
-  const DecodeLayout lay = decode_layout(B, H_q, splits, D);
-  DecArgs args;
-  args.q = (const uint16_t*)q;
-  args.k = (const uint16_t*)k_cache;
-  args.v = (const uint16_t*)v_cache;
-  args.mask = key_padding_mask;
-  args.slopes = alibi_slopes;
-  args.out = (uint16_t*)out;
-  args.lse = lse;
-  args.ws_o = (float*)((char*)workspace + lay.o_offset);
-  args.ws_lse = (float*)((char*)workspace + lay.lse_offset);
-  args.B = B; args.S_k = S_k; args.H_q = H_q; args.H_kv = H_kv; args.G = G;
-  args.n_hg = n_hg; args.splits = splits; args.chunk = chunk;
-  args.scale2 = scale * kLog2e;
-  args.alibi2 = scale != 0.f ? 1.0f / std::fabs(scale) : 0.f;
-  args.arrive = nullptr;
-
-  MergeArgs margs;
-  margs.ws_o = args.ws_o;
-  margs.ws_lse = args.ws_lse;
-  margs.out = (uint16_t*)out;
-  margs.lse = lse;
-  margs.splits = splits;
-
-  const bool m = key_padding_mask != nullptr, al = alibi_slopes != nullptr;
-  hipStream_t hs = (hipStream_t)stream;
-  if (dtype == SA_F16) {
-    if (D == 64) dispatch_decode<F16, 64>(args, margs, (int)nwg, m, al, hs);
-    else dispatch_decode<F16, 128>(args, margs, (int)nwg, m, al, hs);
-  } else {
-    if (D == 64) dispatch_decode<BF16, 64>(args, margs, (int)nwg, m, al, hs);
-    else dispatch_decode<BF16, 128>(args, margs, (int)nwg, m, al, hs);
-  }
-  return launched("decode");
+  return launch_decode(shp, decode_num_splits(B, S_k, H_q, H_kv, cus), workspace, stream);
 }
 
 size_t sa_attn_decode_fused_workspace_size(int B, int H_q, int S_k, int D) {

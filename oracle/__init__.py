@@ -34,12 +34,12 @@ Every function here is pinned by tests that do not go through the oracle's own
 code path (closed forms, invariants, a library routine, brute force); none of
 them is "parity unpinned".
 """
-from .attention import (SPARSE_BLOCK, attention, attention_bwd, attention_ext, attention_probs,
-                        block_sparse_attention, online_attention, merge_states, partial_state,
+from .attention import (SPARSE_BLOCK, attention, attention_bwd, attention_ext,
+                        block_sparse_attention, online_attention, merge_states,
                         alibi_bias, visible)
 from . import brute, philox
 
-__all__ = ["SPARSE_BLOCK", "attention", "attention_bwd", "attention_ext", "attention_probs",
+__all__ = ["SPARSE_BLOCK", "attention", "attention_bwd", "attention_ext",
            "block_sparse_attention", "philox",
            "online_attention", "merge_states",
-           "partial_state", "alibi_bias", "visible", "brute"]
+           "alibi_bias", "visible", "brute"]

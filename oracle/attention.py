@@ -236,22 +236,6 @@ def block_sparse_attention(q, k, v, scale, block_mask, causal=False,
     return out, lse
 
 
-def attention_probs(q, k, scale, b, h, causal=False, key_padding_mask=None,
-                    alibi_slopes=None):
-    """The full probability matrix ``P [S_q, S_k]`` of one (b, h)."""
-    q, k = _f64(q), _f64(k)
-    S_q, H_q = q.shape[1], q.shape[2]
-    S_k, H_kv = k.shape[1], k.shape[2]
-    hk = h // (H_q // H_kv)
-    mrow = None if key_padding_mask is None else np.asarray(key_padding_mask)[b]
-    keep = visible(S_q, S_k, causal, mrow)
-    bias = None
-    if alibi_slopes is not None:
-        bias = alibi_bias(np.asarray(alibi_slopes, np.float64)[h], S_q, S_k)
-    P, _ = _softmax_rows(_scores(q[b, :, h, :], k[b, :, hk, :], scale, keep, bias))
-    return P
-
-
 def online_attention(q, k, v, scale, causal=False, key_padding_mask=None,
                      alibi_slopes=None, block=64):
     """The streaming recurrence of the pages, in float64.
@@ -297,23 +281,6 @@ def online_attention(q, k, v, scale, causal=False, key_padding_mask=None,
                 out[b, :, h, :] = np.where(den[:, None] > 0, num / den[:, None], 0.0)
                 lse[b, h] = np.where(den > 0, run_max + np.log(den), -np.inf)
     return out, lse
-
-
-def partial_state(q, k, v, scale, key_lo, key_hi, causal=False,
-                  key_padding_mask=None, alibi_slopes=None):
-    """Normalised output and lse over the keys ``[key_lo, key_hi)`` only.
-
-    Keys keep their absolute positions (for the causal rule and the bias); the
-    range acts as an extra mask.  This is the per-split state that a split-KV
-    decode writes before merging.
-    """
-    k = _f64(k)
-    B, S_k = k.shape[0], k.shape[1]
-    rng = np.zeros((B, S_k), dtype=bool)
-    rng[:, key_lo:key_hi] = True
-    if key_padding_mask is not None:
-        rng &= np.asarray(key_padding_mask) != 0
-    return attention(q, k, v, scale, causal, rng.astype(np.uint8), alibi_slopes)
 
 
 def merge_states(o_parts, lse_parts):

@@ -195,3 +195,39 @@ def test_bwd_noop_and_workspace(L):
     # One {lse2, Di} float pair per query row.
     assert sa.bwd_workspace_size(2, 14, 4096) == 2 * 14 * 4096 * 8
     assert sa.bwd_workspace_size(-1, 1, 1) == 0
+
+
+BIAS = A + 11 * (1 << 32)
+
+
+def ext(L, q=Q, k=K, v=V, out=O, lse=LSE, B=1, S_q=8, S_k=8, H_q=2, H_kv=2, D=64, scale=0.125,
+        causal=0, mask=None, slopes=None, bias=BIAS, sb=0, sh=0, sq=8, p=0.0, dtype=0):
+    return L.sa_attn_fwd_ext(q, k, v, out, lse, B, S_q, S_k, H_q, H_kv, D, scale, causal, mask,
+                             slopes, bias, sb, sh, sq, p, 0, 0, dtype, None)
+
+
+@pytest.mark.parametrize("kw", [
+    dict(scale=0.0),                    # a bias is added in units of 1/|scale|
+    dict(scale=-0.0),
+    dict(scale=1e-45),                  # 1/|scale| overflows float32
+    dict(bias=None, slopes=SL, scale=0.0),
+    dict(bias=None, slopes=SL, scale=1e-45),
+    dict(p=1.0),
+    dict(sq=6),                         # stride not a multiple of 4
+    dict(bias=BIAS + 4),                # misaligned bias
+    dict(out=BIAS),                     # out overlaps the bias
+])
+def test_ext_rejects(L, kw):
+    assert ext(L, **kw) == sa.SA_ERR_INVALID_ARG
+    assert sa.last_error() != ""
+
+
+def test_bias_scale_rule(L):
+    """With no bias, a zero scale is valid (every score is 0); with one, the
+    tiniest normal scale still has a finite 1/|scale|, so validation passes up
+    to the launch step (no call here reaches a launch: B = 0 stops it after
+    the argument checks)."""
+    assert ext(L, bias=None, scale=0.0, B=0) == sa.SA_OK
+    assert fwd(L, slopes=SL, scale=1e-45) == sa.SA_ERR_INVALID_ARG
+    assert dec(L, slopes=SL, scale=1e-45) == sa.SA_ERR_INVALID_ARG
+    assert "1/|scale|" in sa.last_error()

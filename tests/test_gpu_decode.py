@@ -8,7 +8,7 @@ import pytest
 import torch
 
 import online_softmax_amd as sa
-from parity import assert_lse_close, assert_out_close, oracle_for, to_dev
+from parity import assert_lse_close, assert_out_close, oracle_for, p_rounding, to_dev
 from workloads import WORKLOADS, Workload, make_inputs, to_f64
 
 pytestmark = pytest.mark.gpu
@@ -28,7 +28,8 @@ def check(inp, what=""):
     out, lse = run_decode(inp)
     ref_o, ref_l = oracle_for(inp, causal=False)
     dt = torch.float16 if w.dtype == "fp16" else torch.bfloat16
-    assert_out_close(out, ref_o, dt, what or w.name)
+    assert_out_close(out, ref_o, dt, what or w.name,
+                     p_rounding(oracle_for(inp, causal=False, abs_v=True)[0], dt))
     assert_lse_close(lse, ref_l, what or w.name)
     return out, lse
 
@@ -112,7 +113,8 @@ def test_decode_workspace_reuse():
         torch.cuda.synchronize()
         ref_o, ref_l = oracle_for(inp, causal=False)
         dt = torch.float16 if w.dtype == "fp16" else torch.bfloat16
-        assert_out_close(to_f64(out.cpu()), ref_o, dt, w.name)
+        assert_out_close(to_f64(out.cpu()), ref_o, dt, w.name,
+                         p_rounding(oracle_for(inp, causal=False, abs_v=True)[0], dt))
         assert_lse_close(lse.cpu().double().numpy(), ref_l, w.name)
 
 
@@ -162,7 +164,8 @@ def test_decode_fused_cases(w):
     assert counters_clear(ws)
     ref_o, ref_l = oracle_for(inp, causal=False)
     dt = torch.float16 if w.dtype == "fp16" else torch.bfloat16
-    assert_out_close(out, ref_o, dt, w.name)
+    assert_out_close(out, ref_o, dt, w.name,
+                     p_rounding(oracle_for(inp, causal=False, abs_v=True)[0], dt))
     assert_lse_close(lse, ref_l, w.name)
     # The two-kernel decode agrees (the split counts may differ).
     o2, l2 = run_decode(inp)
@@ -174,7 +177,8 @@ def test_decode_fused_config4():
     print("[decode fused] c4_decode_32k", flush=True)
     out, lse = run_fused(inp)
     ref_o, ref_l = oracle_for(inp, causal=False)
-    assert_out_close(out, ref_o, torch.float16, "c4 fused")
+    assert_out_close(out, ref_o, torch.float16, "c4 fused",
+                     p_rounding(oracle_for(inp, causal=False, abs_v=True)[0], torch.float16))
     assert_lse_close(lse, ref_l, "c4 fused")
 
 
@@ -189,7 +193,8 @@ def test_decode_fused_workspace_reuse():
         assert counters_clear(ws)
         ref_o, ref_l = oracle_for(inp, causal=False)
         dt = torch.float16 if w.dtype == "fp16" else torch.bfloat16
-        assert_out_close(out, ref_o, dt, w.name)
+        assert_out_close(out, ref_o, dt, w.name,
+                         p_rounding(oracle_for(inp, causal=False, abs_v=True)[0], dt))
         assert_lse_close(lse, ref_l, w.name)
 
 

@@ -1,8 +1,9 @@
 """GPU parity of the extended forward (sa_attn_fwd_ext: additive float mask
 and Philox dropout) against the oracle ``oracle.attention_ext``.
 
-Tolerance as for the plain forward: ``5e-3 + ulp_dtype(ref) / 2`` on out,
-1e-3 on lse, -inf matching -inf.  The dropout decisions are integer
+Tolerance as for the plain forward (tests/parity.py): ``5e-3 +
+ulp_dtype(ref) / 2 + u * sum_j w_j |v_j|`` on out, 1e-3 on lse, -inf matching
+-inf.  The dropout decisions are integer
 comparisons of Philox words on both sides, so the dropped outputs are
 compared element by element like any other.  With dropout the product P V
 sums each kept probability, rounded to the input type (relative error at
@@ -10,13 +11,15 @@ most u = 2^-9 for bfloat16, 2^-12 for float16), times 1 / (1 - p): the
 rounding error of an output is then at most u max|v| / (1 - p), and the
 absolute part of the bound becomes ``max(5e-3, u max|v|) / (1 - p)``.
 """
+import dataclasses
+
 import numpy as np
 import pytest
 import torch
 
 import online_softmax_amd as sa
 import oracle
-from parity import OUT_ATOL, assert_lse_close, assert_out_close, half_ulp, to_dev
+from parity import OUT_ATOL, assert_lse_close, assert_out_close, out_bound, p_rounding, to_dev
 from workloads import WORKLOADS, Workload, make_bias, make_inputs, to_f64
 
 pytestmark = pytest.mark.gpu
@@ -56,12 +59,13 @@ def check(inp, bias=None, p=0.0, seed=0, offset=0, rows=None, what=""):
         u = 2.0 ** -9 if w.dtype == "bf16" else 2.0 ** -12
         atol = max(OUT_ATOL, u * float(inp.v.float().abs().max())) / (1.0 - p)
         err = np.abs(out - ref_o)
-        bound = atol + half_ulp(ref_o, dt)
+        bound = out_bound(ref_o, dt) - OUT_ATOL + atol
         print(f"    dropout bound {atol:.3e} + half-ulp; max err {err.max():.3e}; "
               f"worst err/bound {(err / bound).max():.3f}", flush=True)
         assert np.isfinite(out).all() and (err <= bound).all(), f"{what or w.name}: {(err > bound).sum()} beyond"
     else:
-        assert_out_close(out, ref_o, dt, what or w.name)
+        extra = p_rounding(ref_ext(dataclasses.replace(inp, v=inp.v.abs()), bias, p, seed, offset, rows)[0], dt)
+        assert_out_close(out, ref_o, dt, what or w.name, extra)
     assert_lse_close(lse, ref_l, what or w.name)
     return out, lse
 
@@ -148,3 +152,38 @@ def test_ext_rejects():
             sa.attn_fwd_ext(q, k, v, dropout_p=p)
     with pytest.raises(ValueError):
         sa.attn_fwd_ext(q, k, v, attn_bias=torch.zeros(3, 3, device="cuda"))
+
+
+@pytest.mark.parametrize("w,p", [
+    (Workload("keep_f16_d128", 2, 300, 128, 4, 2, 128, "fp16", seed=170), 0.3),
+    (Workload("keep_bf16_d64_causal", 2, 200, 64, 6, 3, 64, "bf16", causal=True, seed=171), 0.5),
+    (Workload("keep_bf16_d128_mask_alibi", 1, 260, 120, 4, 4, 128, "bf16", causal=True, alibi=True,
+              random_tail=20, seed=172), 0.1),
+], ids=lambda c: c.name if isinstance(c, Workload) else str(c))
+def test_dropout_keep_pattern_exact(w, p):
+    """The dropout decisions, bit for bit.  With one-hot values (v_j = e_j,
+    S_k <= D) output column j of row i is P[i, j] * keep[i, j] / (1 - p): it
+    is zero exactly where the kernel dropped the probability (or the key is
+    hidden), so the zero pattern of out[..., :S_k] is compared element by
+    element with the oracle's Philox rule (oracle.philox.keep_mask)."""
+    inp = make_inputs(w)
+    v = torch.zeros_like(inp.v)
+    for j in range(w.S_k):
+        v[:, j, :, j] = 1.0
+    inp.v = v
+    seed, offset = 0x0123456789ABCDEF + w.seed, 7 * w.seed
+    out, lse = run_ext(inp, None, p, seed=seed, offset=offset)
+    ref_o, ref_l = ref_ext(inp, None, p, seed=seed, offset=offset)
+    nz = out[..., :w.S_k] != 0                                 # [B, S_q, H_q, S_k]
+    assert (out[..., w.S_k:] == 0).all()
+    mism = 0
+    for b in range(w.B):
+        vis = oracle.visible(w.S_q, w.S_k, w.causal, None if inp.mask is None else inp.mask[b].numpy())
+        for h in range(w.H_q):
+            keep = oracle.philox.keep_mask(b, h, w.H_q, np.arange(w.S_q), w.S_k, p, seed, offset)
+            mism += int((nz[b, :, h, :] != (keep & vis)).sum())
+    frac = float(nz.mean())
+    print(f"[ext] {w.name}: p={p}, {mism} keep decisions differ, nonzero fraction {frac:.3f}", flush=True)
+    assert mism == 0
+    # And the values themselves, to the dropout bound.
+    check(inp, None, p, seed=seed, offset=offset, what=w.name + " values")

@@ -2,11 +2,9 @@
 
 The oracle is ``oracle.block_sparse_attention``: the page's pseudo-sparse run
 (the block selection expanded into an element mask, then dense attention).
-Tolerance as for the dense forward: ``5e-3 + ulp_dtype(ref) / 2`` on out,
-1e-3 on lse, -inf matching -inf; with ALiBi the out bound adds the
-probability-rounding term ``u * sum_j w_j |v_j|`` (``parity.p_rounding``): a
-causal ALiBi sweep starts on the diagonal, and the rows of steep-slope heads
-put their weight on a few keys.  Block selections come from
+Tolerance as for the dense forward (tests/parity.py): ``5e-3 +
+ulp_dtype(ref) / 2 + u * sum_j w_j |v_j|`` on out, 1e-3 on lse, -inf
+matching -inf.  Block selections come from
 ``workloads.make_block_mask`` (sink and window blocks always, the rest at
 random) or are built here for the edge cases.
 """
@@ -16,7 +14,7 @@ import torch
 
 import online_softmax_amd as sa
 import oracle
-from parity import OUT_ATOL, assert_lse_close, assert_out_close, half_ulp, p_rounding, to_dev
+from parity import assert_lse_close, assert_out_close, out_bound, p_rounding, to_dev
 from workloads import WORKLOADS, Workload, make_block_mask, make_inputs, to_f64
 
 pytestmark = pytest.mark.gpu
@@ -50,11 +48,7 @@ def check(inp, bm, rows=None, what=""):
     if rows is not None:
         out, lse = out[:, rows], lse[:, :, rows]
     dt = torch.float16 if w.dtype == "fp16" else torch.bfloat16
-    # Under causal ALiBi the sweep starts on the diagonal, so the rows of the
-    # steep-slope heads (weight concentrated on a few keys) carry the
-    # probability-rounding term in full.
-    extra = p_rounding(ref_sparse(inp, bm, rows, abs_v=True)[0], dt) if inp.slopes is not None else None
-    assert_out_close(out, ref_o, dt, what or w.name, extra)
+    assert_out_close(out, ref_o, dt, what or w.name, p_rounding(ref_sparse(inp, bm, rows, abs_v=True)[0], dt))
     assert_lse_close(lse, ref_l, what or w.name)
     return out, lse
 
@@ -91,8 +85,8 @@ def test_sparse_all_selected_is_dense(w):
     dense = to_f64(do.cpu())
     dt = torch.float16 if w.dtype == "fp16" else torch.bfloat16
     bm_all = torch.ones((w.B, w.H_q, nbq, nbk), dtype=torch.uint8)
-    extra = p_rounding(ref_sparse(inp, bm_all, abs_v=True)[0], dt) if inp.slopes is not None else 0.0
-    assert (np.abs(out - dense) <= 2 * (OUT_ATOL + half_ulp(dense, dt) + extra)).all()
+    extra = p_rounding(ref_sparse(inp, bm_all, abs_v=True)[0], dt)
+    assert (np.abs(out - dense) <= 2 * out_bound(dense, dt, extra)).all()
     assert np.abs(lse - dl.cpu().double().numpy()).max() <= 1e-4
 
 

@@ -287,11 +287,31 @@ def test_online_recurrence_reaches_definition(block):
 
 
 def test_prob_matrix_rows():
+    """Rows of P sum to 1 over the visible keys and are 0 elsewhere.  P is read
+    off ``attention`` itself: with one-hot value rows (v_j = e_j, S_k <= D)
+    out[i, :S_k] is row i of P, so this pins the probabilities the outputs
+    are built from, across GQA heads, ALiBi and padding."""
     rng = np.random.default_rng(13)
-    q, k = rnd(rng, 1, 12, 2, 4), rnd(rng, 1, 12, 1, 4)
-    P = oracle.attention_probs(q, k, 0.5, 0, 1, causal=True, alibi_slopes=np.array([0.1, 0.3]))
-    assert np.abs(P.sum(axis=1) - 1).max() <= 1e-12
-    assert (np.triu(P, 1) == 0).all()
+    B, S, H_q, H_kv, D = 2, 12, 4, 2, 16
+    q, k = rnd(rng, B, S, H_q, D), rnd(rng, B, S, H_kv, D)
+    v = np.zeros((B, S, H_kv, D))
+    for j in range(S):
+        v[:, j, :, j] = 1.0
+    mask = np.ones((B, S), np.uint8)
+    mask[1, 9:] = 0
+    slopes = np.array([0.1, 0.3, 0.0, 0.7])
+    out, lse = oracle.attention(q, k, v, 0.3, True, mask, slopes)
+    for b in range(B):
+        keep = np.tril(np.ones((S, S), bool)) & (mask[b] != 0)[None, :]
+        for h in range(H_q):
+            P = out[b, :, h, :S]
+            assert np.abs(P.sum(axis=1) - 1).max() <= 1e-12
+            assert (P[~keep] == 0).all() and (P[keep] > 0).all()
+            assert (out[b, :, h, S:] == 0).all()
+            # P[i, j] = exp(s[i, j] - lse[i]) for each visible key.
+            hk = h // (H_q // H_kv)
+            s = 0.3 * q[b, :, h] @ k[b, :, hk].T - slopes[h] * np.abs(np.arange(S)[:, None] - np.arange(S)[None, :])
+            assert close(np.log(P[keep]), (s - lse[b, h][:, None])[keep], 1e-12)
 
 
 def test_rows_subset_matches_full():
