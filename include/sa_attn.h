@@ -193,6 +193,27 @@ int sa_attn_decode(const void* q, const void* k_cache, const void* v_cache,
                    int dtype, void* workspace, size_t workspace_bytes, sa_stream_t stream);
 
 /*
+ * sa_attn_decode without a workspace argument, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops
+ * and harnesses that forbid allocation.  Same arguments, rules, kernels and
+ * results as sa_attn_decode; the decode's partial results live in a 16 MiB
+ * scratch array inside this library instead (each GPU holds its own copy
+ * from the library's load until the process ends).  The call allocates and
+ * frees nothing.
+ *
+ * Every call on one GPU shares that GPU's scratch: calls that may overlap on
+ * one GPU (different streams with no ordering between them) race and must
+ * not be issued.  A shape whose partial results exceed the scratch
+ * (B * H_q * splits * (D + 1) * 4 bytes, splits as sa_attn_decode_num_splits)
+ * returns SA_ERR_UNSUPPORTED with a message; use sa_attn_decode with a
+ * workspace for it.  Other errors as sa_attn_decode.
+ */
+int sa_attn_decode_noalloc(const void* q, const void* k_cache, const void* v_cache,
+                           void* out, float* lse, int B, int S_k, int H_q, int H_kv, int D,
+                           float scale, const uint8_t* key_padding_mask, const float* alibi_slopes,
+                           int dtype, sa_stream_t stream);
+
+/*
  * Bytes of device workspace sa_attn_decode_fused needs: 65536 bytes of
  * arrival counters followed by sa_attn_decode's partial area.  Pure host
  * arithmetic; returns 0 when a size is negative or the result would overflow.

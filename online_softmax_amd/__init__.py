@@ -14,6 +14,7 @@ Functions keep the names of the C entry points:
 * ``attn_decode(q, k_cache, v_cache, scale=None, key_padding_mask=None,
   alibi_slopes=None, out=None, lse=None, workspace=None, return_lse=True)``
 * ``decode_workspace_size(B, H_q, S_k, D)`` and ``decode_num_splits(...)``
+* ``attn_decode_noalloc(...)`` (no workspace: the library's own scratch)
 * ``attn_decode_fused(...)`` (one kernel) and
   ``decode_fused_workspace(B, H_q, S_k, D, device)``
 * ``attn_fwd_block_sparse(q, k, v, block_mask, causal=False, ...)``
@@ -49,6 +50,7 @@ SIGNATURES = {
                              _FP, _I64, _I64, _I64, _D, _U64, _U32, _I, _VP]),
     "sa_attn_decode_workspace_size": (_SZ, [_I, _I, _I, _I]),
     "sa_attn_decode": (_I, [_VP, _VP, _VP, _VP, _FP, _I, _I, _I, _I, _I, _F, _U8P, _FP, _I, _VP, _SZ, _VP]),
+    "sa_attn_decode_noalloc": (_I, [_VP, _VP, _VP, _VP, _FP, _I, _I, _I, _I, _I, _F, _U8P, _FP, _I, _VP]),
     "sa_attn_decode_num_splits": (_I, [_I, _I, _I, _I, _I]),
     "sa_attn_decode_fused_num_splits": (_I, [_I, _I, _I, _I, _I]),
     "sa_attn_decode_fused_workspace_size": (_SZ, [_I, _I, _I, _I]),
@@ -324,6 +326,23 @@ def attn_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
                               B, S_k, H_q, H_kv, D, sc, _ptr(mask), _ptr(alibi_slopes),
                               _DTYPE[q.dtype], workspace.data_ptr(),
                               workspace.numel() * workspace.element_size(), _stream(dev))
+    _check(st)
+    return (out, lse) if return_lse else out
+
+
+def attn_decode_noalloc(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                        scale: Optional[float] = None, key_padding_mask: Optional[torch.Tensor] = None,
+                        alibi_slopes: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
+                        lse: Optional[torch.Tensor] = None, return_lse: bool = True):
+    """``attn_decode`` through ``sa_attn_decode_noalloc``: the library keeps
+    the partial results in its own scratch, so no workspace is passed and the
+    C call allocates nothing (pass ``out`` and ``lse`` to allocate nothing
+    here either).  Calls that may overlap on one GPU must not be issued."""
+    dev, (B, S_k, H_q, H_kv, D), mask, out, lse, sc = _decode_prepare(
+        q, k_cache, v_cache, key_padding_mask, alibi_slopes, out, lse, return_lse, scale)
+    st = lib().sa_attn_decode_noalloc(q.data_ptr(), _ptr(k_cache), _ptr(v_cache), out.data_ptr(), _ptr(lse),
+                                      B, S_k, H_q, H_kv, D, sc, _ptr(mask), _ptr(alibi_slopes),
+                                      _DTYPE[q.dtype], _stream(dev))
     _check(st)
     return (out, lse) if return_lse else out
 

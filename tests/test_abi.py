@@ -231,3 +231,14 @@ def test_bias_scale_rule(L):
     assert fwd(L, slopes=SL, scale=1e-45) == sa.SA_ERR_INVALID_ARG
     assert dec(L, slopes=SL, scale=1e-45) == sa.SA_ERR_INVALID_ARG
     assert "1/|scale|" in sa.last_error()
+
+
+def test_decode_noalloc_argument_checks(L):
+    """The allocation-free decode checks its arguments before any HIP call."""
+    def call(q=Q, k=K, v=V, out=O, lse=LSE, B=1, S_k=100, H_q=4, H_kv=2, D=64, scale=0.125, dtype=0):
+        return L.sa_attn_decode_noalloc(q, k, v, out, lse, B, S_k, H_q, H_kv, D, scale, None, None, dtype, None)
+    assert call(B=0, q=None, out=None) == sa.SA_OK
+    assert call(q=None) == sa.SA_ERR_INVALID_ARG
+    assert call(out=Q) == sa.SA_ERR_INVALID_ARG
+    assert call(D=96) == sa.SA_ERR_UNSUPPORTED
+    assert call(H_q=5) == sa.SA_ERR_INVALID_ARG
