@@ -63,10 +63,15 @@ HBM_PEAK_GBS = 8000.0       # MI355X HBM3E bandwidth (published)
 DECODE_ROTATION_BYTES = 768 << 20
 PROFILES = ROOT / "profiles"
 # Sources each kernel is built from: a traffic figure measured on other sources is stale.
+# Each mode of an entry point has its own kernel instances and so its own
+# counter summary (``profiles/<tag>_<workload>_traffic.txt``).
 KERNEL_SOURCES = {
-    "fwd_kernel": ["common.hpp", "host_logic.hpp", "prefill.hpp", "sa_attn.hip"],
-    "decode_kernel": ["common.hpp", "host_logic.hpp", "decode.hpp", "sa_attn.hip"],
-    "bwd_kernels": ["common.hpp", "host_logic.hpp", "backward.hpp", "sa_attn_bwd.hip"],
+    "fwd_kernel": ["common.hpp", "host_logic.hpp", "launch.hpp", "prefill.hpp", "sa_attn.hip"],
+    "fwd_kernel_sparse": ["common.hpp", "host_logic.hpp", "launch.hpp", "prefill.hpp", "sa_attn_sparse.hip"],
+    "fwd_kernel_ext": ["common.hpp", "host_logic.hpp", "launch.hpp", "prefill.hpp", "sa_attn_ext.hip"],
+    "decode_kernel": ["common.hpp", "host_logic.hpp", "launch.hpp", "decode.hpp", "sa_attn.hip"],
+    "decode_kernel_fused": ["common.hpp", "host_logic.hpp", "launch.hpp", "decode.hpp", "sa_attn.hip"],
+    "bwd_kernels": ["common.hpp", "host_logic.hpp", "launch.hpp", "backward.hpp", "sa_attn_bwd.hip"],
 }
 
 STEPS = {
@@ -146,7 +151,9 @@ def source_sha(kernel):
 
 
 def read_traffic(kernel, workload):
-    """HBM bytes per launch from a committed counter summary, if still current."""
+    """HBM bytes per launch from the committed counter summary of this kernel
+    tag (entry-point mode) and workload, if it exists and its sources are
+    unchanged; otherwise None."""
     p = PROFILES / f"{kernel}_{workload}_traffic.txt"
     if not p.exists():
         return None
@@ -255,8 +262,10 @@ def cpu_baseline(parts, budget_s):
     flops = 0
     secs = 0.0
     samples = []
+    part_secs = []
     per_part = budget_s / len(parts)
     for p in parts:
+        secs_before = secs
         w = p.w
         inp = make_inputs(w)
         q, k, v = to_f64(inp.q), to_f64(inp.k), to_f64(inp.v)
@@ -267,6 +276,7 @@ def cpu_baseline(parts, budget_s):
             f, t, desc = _cpu_bwd_sample(p, inp, q, k, v, mask, sl, per_part)
             flops, secs = flops + f, secs + t
             samples.append(desc)
+            part_secs.append(secs - secs_before)
             continue
         # Grow an evenly spaced row sample until the part has used its budget.
         n_rows, used, done_rows = 1, 0.0, 0
@@ -304,9 +314,12 @@ def cpu_baseline(parts, budget_s):
             done_rows += n
             n_rows *= 2
         secs += used
+        part_secs.append(secs - secs_before)
         samples.append(f"{w.name}: {done_rows} of {w.S_q} query rows x all batches and heads")
     return {"value": flops / secs / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
-            "sample": "; ".join(samples) + f" ({secs:.1f} s of float64 numpy)"}
+            "sample": "; ".join(samples) + f" ({secs:.1f} s of float64 numpy)",
+            "part_seconds": {p.w.name: round(t, 2) for p, t in zip(parts, part_secs)},
+            "host_cpus": os.cpu_count(), "cpu_model": cpu_model()}
 
 
 def _cpu_bwd_sample(p, inp, q, k, v, mask, sl, budget_s):
@@ -329,6 +342,73 @@ def _cpu_bwd_sample(p, inp, q, k, v, mask, sl, budget_s):
         flops += 10 * w.D * visible_pairs(OneRow(w), [inp.tails[b]] if inp.tails else [])
         n += 1
     return flops, used, f"{w.name} backward: {n} of {w.B * w.H_q} (batch row, head) pairs, whole rows"
+
+
+def cpu_model():
+    """The host CPU's model name (as lscpu reports it), from /proc/cpuinfo."""
+    try:
+        for line in Path("/proc/cpuinfo").read_text().splitlines():
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_table():
+    """Wall time of the float64 oracle per configuration on this host: with the
+    BLAS thread count the process has, and with one thread for the small
+    configurations 1, 2 and 4.  Inputs are generated before the clock starts.
+    Configurations 3 and 5 are timed on whole (batch, head) pairs until 20 s
+    have passed and scaled to all of them (the oracle's cost is the same for
+    every pair of a configuration)."""
+    import numpy as np
+    import oracle
+    from threadpoolctl import threadpool_info, threadpool_limits
+    from workloads import WORKLOADS, make_inputs, to_f64
+    threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    rows = []
+    for name in ["c1_fwd_256", "c2_causal_pad16", "c3_causal_4096", "c3_noncausal_4096",
+                 "c4_decode_32k", "c5_alibi_8192"]:
+        w = WORKLOADS[name]
+        inp = make_inputs(w)
+        q, k, v = to_f64(inp.q), to_f64(inp.k), to_f64(inp.v)
+        mask = None if inp.mask is None else inp.mask.numpy()
+        sl = None if inp.slopes is None else inp.slopes.numpy()
+        causal = w.causal and not w.decode
+        small = name in ("c1_fwd_256", "c2_causal_pad16", "c4_decode_32k")
+
+        def whole():
+            t0 = time.perf_counter()
+            oracle.attention(q, k, v, w.scale, causal=causal, key_padding_mask=mask, alibi_slopes=sl)
+            return time.perf_counter() - t0
+
+        def by_pairs(budget=20.0):
+            G = w.H_q // w.H_kv
+            used, n = 0.0, 0
+            while used < budget and n < w.B * w.H_q:
+                b, h = n % w.B, (n // w.B) % w.H_q
+                t0 = time.perf_counter()
+                oracle.attention(q[b:b + 1, :, h:h + 1], k[b:b + 1, :, h // G:h // G + 1],
+                                 v[b:b + 1, :, h // G:h // G + 1], w.scale, causal=causal,
+                                 key_padding_mask=None if mask is None else mask[b:b + 1],
+                                 alibi_slopes=None if sl is None else sl[h:h + 1])
+                used += time.perf_counter() - t0
+                n += 1
+            return used * (w.B * w.H_q) / n, n
+
+        if small:
+            whole()  # first call: BLAS thread start-up, outside the clock
+            t_all = whole()
+            with threadpool_limits(1):
+                t_one = whole()
+            rows.append({"config": name, "all_threads_s": round(t_all, 3), "one_thread_s": round(t_one, 3),
+                         "timed": "whole"})
+        else:
+            t_all, n = by_pairs()
+            rows.append({"config": name, "all_threads_s": round(t_all, 2), "one_thread_s": None,
+                         "timed": f"{n} of {w.B * w.H_q} (batch, head) pairs, scaled"})
+    return {"blas_threads": threads, "host_cpus": os.cpu_count(), "cpu_model": cpu_model(), "rows": rows}
 
 
 class OneRow:
@@ -365,12 +445,18 @@ def main():
     ap.add_argument("--print-source-sha", action="store_true",
                     help="print the source hash of each kernel (recorded with counter summaries) and exit")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
+    ap.add_argument("--cpu-table", action="store_true",
+                    help="instead of the hot path, print the float64 oracle's wall time per configuration "
+                         "on this host (all BLAS threads, and one thread for configurations 1, 2 and 4)")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="instead of the hot path, time a plain device-to-device copy of this many "
                          "MiB (the reference kernel for scaling HBM byte counters)")
     args = ap.parse_args()
     if args.print_source_sha:
         print(json.dumps({k: source_sha(k) for k in KERNEL_SOURCES}))
+        return
+    if args.cpu_table:
+        print(json.dumps(cpu_table()), flush=True)
         return
     if args.gpus != 1:
         print(f"bench.py runs on exactly one GPU (asked for {args.gpus}); multi-GPU sharding is "
@@ -473,7 +559,8 @@ def main():
         ach = p.flops / (t * 1e-3) / 1e12
         result["roofline"] = {"bound": "mfma", "achieved": round(ach, 2), "peak": MFMA_PEAK_TFLOPS,
                               "unit": "TFLOP/s", "frac": round(ach / MFMA_PEAK_TFLOPS, 4),
-                              "traffic": read_traffic("fwd_kernel", p.w.name),
+                              "traffic": read_traffic("fwd_kernel" + ("_sparse" if p.sparse else "")
+                                                      + ("_ext" if p.ext else ""), p.w.name),
                               "kernel": "fwd_kernel" + (" (block-sparse)" if p.sparse else "")
                                         + (" (bias + dropout)" if p.ext else ""),
                               "workload": p.w.name + (" block-sparse" if p.sparse else "")
@@ -485,7 +572,7 @@ def main():
         p, t = decode[0]
         gbs = kv_bytes(p.w) / (t * 1e-3) / 1e9
         dec = {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-               "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": read_traffic("decode_kernel", p.w.name),
+               "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": read_traffic("decode_kernel" + ("_fused" if p.fused else ""), p.w.name),
                "kernels": "decode_kernel (single-kernel mode)" if p.fused else "decode_kernel + decode_merge_kernel",
                "workload": p.w.name + (" single-kernel" if p.fused else ""),
                "avg_call_us": round(t * 1e3, 2), "kv_bytes_per_call": kv_bytes(p.w)}
