@@ -339,17 +339,22 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(DecArgs a) {
     }
   }
   if constexpr (FUSED) {
-    // Count this split on the head group's arrival counter once wave 0's
-    // partial stores have completed; the last of the group's splits to
-    // arrive resets the counter and merges them all.
+    // Count this split on the head group's arrival counter; the last of the
+    // group's splits to arrive resets the counter and merges them all.  The
+    // partials were stored by wave 0, the wave of thread 0, so they precede
+    // its count in program order: the count releases them at agent scope.
+    // The last arriver then acquires (agent scope) every other split's
+    // partials, which the barrier hands to the whole workgroup.
     __shared__ int s_last;
     __syncthreads();
     if (tid == 0) {
-      __builtin_amdgcn_s_waitcnt(0);
       unsigned* cnt = a.arrive + grp;
-      const bool last = __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+      const bool last = __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT) ==
                         (unsigned)a.splits - 1u;
-      if (last) __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (last) {
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+        __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
       s_last = last;
     }
     __syncthreads();
