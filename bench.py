@@ -15,10 +15,18 @@ A step is one pass of the whole hot path over resident synthetic inputs:
 
 ``value`` is the step's algorithmic FLOPs (4 * D * H_q * visible query-key
 pairs, summed over the parts) divided by the measured time per step, in
-TFLOP/s.  HIP events recorded on the launch stream time each part; the
-``roofline`` object is for the dominant kernel (the prefill kernel) against
-the 2.5 PFLOP/s dense bf16 matrix peak, and ``decode`` carries the decode
-part's key/value read bandwidth against 8 TB/s.  ``cpu_baseline`` times the
+TFLOP/s; HIP events on the launch stream bracket the K timed steps, with no
+event between the parts of a step.  Each part is then timed on its own: K
+calls back to back between two events, after the warm-up count of calls
+(and, for a part shorter on the device than its host launch, the decode, a
+lead of matrix multiplies so that the device never waits for the host).
+Ahead of the warm-up and timed steps bench.py queues at least 40 ms of
+4096^3 fp16 matrix multiplies, so that the device never waits for the host
+and the timed steps run at the clock sustained work holds, not in the ramp
+that follows an idle gap.
+The ``roofline`` object is for the dominant kernel (the prefill kernel)
+against the 2.5 PFLOP/s dense bf16 matrix peak, and ``decode`` carries the
+decode part's key/value read bandwidth against 8 TB/s.  ``cpu_baseline`` times the
 float64 CPU oracle on a bounded sample of the same workloads on this host.
 
 The ``*_sparse`` workload times the block-sparse forward
@@ -61,6 +69,8 @@ HBM_PEAK_GBS = 8000.0       # MI355X HBM3E bandwidth (published)
 # Decode steps rotate over copies of the cache totalling at least this many
 # bytes (three times the 256 MB last-level cache), and at least 8 copies.
 DECODE_ROTATION_BYTES = 768 << 20
+# Least device time of the matrix-multiply lead queued ahead of the timed steps.
+PREHEAT_MS = 40.0
 PROFILES = ROOT / "profiles"
 # Sources each kernel is built from: a traffic figure measured on other sources is stale.
 # Each mode of an entry point has its own kernel instances and so its own
@@ -474,10 +484,7 @@ def main():
 
     # Warm-up: the first steps one at a time (first use of every kernel, and
     # the host's time per step), the rest queued directly ahead of the timed
-    # steps.  After an idle gap or a run of matrix multiplies the c5 prefill
-    # took up to 1.48 ms on its first launches and fell steadily to 1.07 ms
-    # over about twenty; warm-up steps that end where the timed ones begin
-    # leave the GPU in the state this workload keeps it in.
+    # steps, after the lead below.
     n_sync = min(args.warmup, 3)
     host_s = []
     for _ in range(n_sync):
@@ -501,27 +508,62 @@ def main():
     torch.cuda.synchronize()
     mm_ms = max(e0.elapsed_time(e1), 1e-3)
     host_step_s = sorted(host_s)[len(host_s) // 2] if host_s else 1e-3
-    lead_ms = 1.5 * (args.warmup - n_sync + args.steps) * 1e3 * host_step_s + 1.0
-    n_lead = min(int(math.ceil(lead_ms / mm_ms)), 20000)
 
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(parts) + 1)] for _ in range(args.steps)]
+    def lead(n_calls, host_s_per_call, min_ms=0.0):
+        lead_ms = max(1.5 * n_calls * 1e3 * host_s_per_call + 1.0, min_ms)
+        n = min(int(math.ceil(lead_ms / mm_ms)), 20000)
+        for _ in range(n):
+            torch.mm(a, a)
+        return n
+
+    # Timed steps: events only before the first and after the last, so that
+    # no event marker sits between the parts of a step.  The lead ahead of
+    # them is at least PREHEAT_MS of matrix multiplies: after an idle gap the
+    # c5 prefill took 1.2-1.4 ms on its first launches and settled at
+    # 1.09 ms only after about 25 (the GPU's clock under sustained load),
+    # while right after 600 matrix multiplies it settled within 5; so the
+    # timed steps run in the state that sustained work keeps the GPU in,
+    # whatever the warm-up count.
     t0 = time.perf_counter()
-    for _ in range(n_lead):
-        torch.mm(a, a)
+    n_lead = lead(args.warmup - n_sync + args.steps, host_step_s, PREHEAT_MS)
     for _ in range(args.warmup - n_sync):
         for p in parts:
             p.run()
+    e0.record(stream)
     for s in range(args.steps):
-        ev[s][0].record(stream)
-        for i, p in enumerate(parts):
+        for p in parts:
             p.run()
-            ev[s][i + 1].record(stream)
+    e1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    part_ms = [sum(ev[s][i].elapsed_time(ev[s][i + 1]) for s in range(args.steps)) / args.steps
-               for i in range(len(parts))]
-    step_ms = sum(ev[s][0].elapsed_time(ev[s][-1]) for s in range(args.steps)) / args.steps
-    ms_per_step = max(step_ms, 0.0)
+    ms_per_step = max(e0.elapsed_time(e1) / args.steps, 0.0)
+
+    # Each part's own time per call, right after the timed steps: the same
+    # number of calls back to back between two events, after the warm-up
+    # count of calls.  A part that takes less device time per call than the
+    # host needs to launch it (the decode) gets a lead first; the prefill,
+    # which the lead's matrix multiplies would slow for its next launches,
+    # does not need one.
+    part_ms = []
+    for p in parts:
+        torch.cuda.synchronize()
+        t_host = time.perf_counter()
+        e0.record(stream)
+        for _ in range(3):
+            p.run()
+        e1.record(stream)
+        host_call_s = (time.perf_counter() - t_host) / 3
+        torch.cuda.synchronize()
+        if e0.elapsed_time(e1) / 3 < 2e3 * host_call_s:
+            lead(args.warmup + args.steps, host_call_s)
+        for _ in range(args.warmup):
+            p.run()
+        e0.record(stream)
+        for _ in range(args.steps):
+            p.run()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        part_ms.append(e0.elapsed_time(e1) / args.steps)
 
     total_flops = sum(p.flops for p in parts)
     value = total_flops / (ms_per_step * 1e-3) / 1e12
