@@ -54,8 +54,10 @@ def check(inp, what=""):
         assert np.isfinite(g).all(), f"{what or w.name}: non-finite {name}"
         err = np.abs(g - r)
         bound = GRAD_ATOL[w.dtype] + half_ulp(r, dt)
+        fp16_bound = GRAD_ATOL["fp16"] + half_ulp(r, dt)
         print(f"    {name}: max abs err {err.max(initial=0):.3e}  max |ref| {np.abs(r).max(initial=0):.3e}  "
-              f"worst err/bound {np.max(err / bound, initial=0):.3f}", flush=True)
+              f"worst err/bound {np.max(err / bound, initial=0):.3f} "
+              f"(against the float16 bound: {np.max(err / fp16_bound, initial=0):.3f})", flush=True)
         assert (err <= bound).all(), f"{what or w.name}: {int((err > bound).sum())} {name} elements beyond bound"
     return got
 
