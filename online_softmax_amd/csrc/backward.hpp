@@ -48,9 +48,11 @@ struct BwdArgs {
   float alibi2;         // 1 / |scale|
   int nqb;              // query blocks of 128 rows per (batch, head)   (dq kernel)
   int nkb;              // key blocks of 128 keys per (batch, KV head)  (dk/dv kernel)
-  // dq kernel: the number of CUs when its causal grid is resident at two
-  // workgroups per CU (workgroups j and j + pair_ncu share a CU), else 0.
+  // dq and dk/dv kernels: the number of CUs when the kernel's causal grid is
+  // resident at two workgroups per CU (workgroups j and j + pair_ncu share a
+  // CU), else 0.
   int pair_ncu;
+  int pair_ncu_kv;
 };
 
 template <int D>
@@ -327,7 +329,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
 // dk, dv: 4 waves x 32 keys; tiles of 32 query rows of every query head of
 // the KV head.
 template <class T, int D, bool CAUSAL, bool MASK, bool ALIBI>
-__global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a) {
+__global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdArgs a) {
   constexpr int NW = 4, BK = 32 * NW, BQ = 32, NS = 2;
   constexpr int KK = D / 16, DB = D / 32;
   constexpr int NI = BQ * D * 2 / 1024;  // 1 KiB copies per tensor per tile (all by one wave each)
@@ -338,9 +340,22 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int li = lane & 31, g = lane >> 5;
-  const int item = xcd_contiguous(blockIdx.x, a.B * a.H_kv * a.nkb);
-  const int bk = item / a.nkb, kbi = item - bk * a.nkb;
-  const int kblk = kbi;  // under the causal rule the first key blocks carry the most rows
+  int bk, kblk;
+  if (CAUSAL && a.pair_ncu_kv > 0) {
+    // The whole grid is resident, two workgroups per CU: workgroups j and
+    // j + pair_ncu_kv share a CU and take key blocks lvl and nkb - 1 - lvl of
+    // one KV head, so that every CU carries the same number of query rows.
+    const int ncu = a.pair_ncu_kv, j = blockIdx.x;
+    const int p = j < ncu ? j : j - ncu;
+    const int nbk = a.B * a.H_kv;
+    bk = p % nbk;
+    const int lvl = p / nbk;
+    kblk = j < ncu ? lvl : a.nkb - 1 - lvl;
+  } else {
+    const int item = xcd_contiguous(blockIdx.x, a.B * a.H_kv * a.nkb);
+    bk = item / a.nkb;
+    kblk = item - bk * a.nkb;  // under the causal rule the first key blocks carry the most rows
+  }
   const int b = bk / a.H_kv, hk = bk - b * a.H_kv;
   const int k0 = kblk * BK;
   const int kj = k0 + 32 * w + li;  // this lane's key
@@ -357,13 +372,15 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a) {
 
   const size_t qrs = (size_t)a.H_q * D;  // q / dout row stride
   // Tile copies: wave 0 copies Q, wave 1 copies dO, wave 2 the rows' {lse2, Di}.
-  uint32_t toff[NI];
-#pragma unroll
-  for (int u = 0; u < NI; ++u) {
-    const int byte = u * 1024 + 16 * lane;
+  // Copy u of a lane fills LDS row r, position p, from global chunk
+  // p ^ f(r); the offsets are recomputed at each tile (from a lane index the
+  // compiler cannot see through) rather than held in registers for the whole
+  // sweep.
+  auto toff = [&](const int ln, const int u) -> uint32_t {
+    const int byte = u * 1024 + 16 * ln;
     const int r = byte / (2 * D), p = (byte % (2 * D)) / 16;
-    toff[u] = (uint32_t)(r * qrs * 2 + 16 * (p ^ bwd_swizzle<D>(r)));
-  }
+    return (uint32_t)(r * qrs * 2 + 16 * (p ^ bwd_swizzle<D>(r)));
+  };
   auto issue = [&](int it) {
     const int gi = it / per_head, qt = qt0 + (it - gi * per_head);
     const int h = hk * a.G + gi;
@@ -373,8 +390,10 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a) {
       const uint16_t* base = (w == 0 ? a.q : a.dout) + (((size_t)b * a.S_q + i0) * a.H_q + h) * D;
       const auto r = buffer_rsrc(base, (uint32_t)((rows - 1) * qrs * 2 + 2 * D));
       uint16_t* dst = w == 0 ? Qs[buf] : Os[buf];
+      int ln = lane;
+      __asm__ volatile("" : "+v"(ln));
 #pragma unroll
-      for (int u = 0; u < NI; ++u) load_lds16(r, dst + u * 512, toff[u]);
+      for (int u = 0; u < NI; ++u) load_lds16(r, dst + u * 512, toff(ln, u));
     } else if (w == 2) {
       // BQ float2 = 256 bytes: 16 lanes of 16 bytes (the others would write
       // past Ls[buf]); rows past S_q read zero.
@@ -462,20 +481,28 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a) {
       } else {
         s = (f32x16){};
       }
-      // All of the tile's Q and dO fragments are read before the first MFMA
-      // (one wave per SIMD: nothing else would hide the LDS latency).
-      u32x4 qa[KK], oa[KK];
+      // The tile's Q and dO fragments, read RA k-steps ahead of their MFMAs
+      // (two waves per SIMD hide the rest of the LDS latency).
+      constexpr int RA = 1;
+      auto frag = [&](const uint16_t* t, int kk) -> u32x4 {
+        return *(const u32x4*)&t[li * D + 8 * ((2 * kk + g) ^ rsw)];
+      };
+      u32x4 qa[RA], oa[RA];
 #pragma unroll
-      for (int kk = 0; kk < KK; ++kk) {
-        const int off16 = li * D + 8 * ((2 * kk + g) ^ rsw);
-        qa[kk] = *(const u32x4*)&qt_[off16];
-        oa[kk] = *(const u32x4*)&ot_[off16];
+      for (int kk = 0; kk < RA; ++kk) {
+        qa[kk] = frag(qt_, kk);
+        oa[kk] = frag(ot_, kk);
       }
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int kk = 0; kk < KK; ++kk) {
-        s = T::mma(qa[kk], kreg[kk], s);
-        dp = T::mma(oa[kk], vreg[kk], dp);
+        s = T::mma(qa[kk % RA], kreg[kk], s);
+        dp = T::mma(oa[kk % RA], vreg[kk], dp);
+        if (kk + RA < KK) {
+          qa[kk % RA] = frag(qt_, kk + RA);
+          oa[kk % RA] = frag(ot_, kk + RA);
+        }
+        __builtin_amdgcn_sched_barrier(0);
       }
       // Rows' lse2 and Di: registers r = 4 c .. 4 c + 3 hold rows 8 c + 4 g + 0..3.
       uint32_t pk[8], dk_[8];
@@ -505,28 +532,30 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a) {
         dk_[2 * c] = T::pack2(ds[0], ds[1]);
         dk_[2 * c + 1] = T::pack2(ds[2], ds[3]);
       }
-      // dV^T += dO^T P and dK^T += Q^T dS over two 16-row steps, each step's
-      // transposed fragments read before its MFMAs.
+      // dV^T += dO^T P and dK^T += Q^T dS over two 16-row steps; the
+      // transposed fragments of d block i + 1 are read under the MFMAs of
+      // block i.
+      auto trf = [&](const uint16_t* t, int i) -> u32x4 {
+        const int ks = i / DB, db = i % DB;
+        const u32x2 lo = lds_read_tr(t + 16 * ks * D + tofs[0][db]);
+        const u32x2 hi = lds_read_tr(t + 16 * ks * D + tofs[1][db]);
+        return (u32x4){lo[0], lo[1], hi[0], hi[1]};
+      };
+      u32x4 ov = trf(ot_, 0), qv = trf(qt_, 0);
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
+      for (int i = 0; i < 2 * DB; ++i) {
+        const int ks = i / DB, db = i % DB;
         const u32x4 bp = {pk[4 * ks], pk[4 * ks + 1], pk[4 * ks + 2], pk[4 * ks + 3]};
         const u32x4 bd = {dk_[4 * ks], dk_[4 * ks + 1], dk_[4 * ks + 2], dk_[4 * ks + 3]};
-        u32x4 ov[DB], qv[DB];
-#pragma unroll
-        for (int db = 0; db < DB; ++db) {
-          const u32x2 olo = lds_read_tr(ot_ + 16 * ks * D + tofs[0][db]);
-          const u32x2 ohi = lds_read_tr(ot_ + 16 * ks * D + tofs[1][db]);
-          const u32x2 qlo = lds_read_tr(qt_ + 16 * ks * D + tofs[0][db]);
-          const u32x2 qhi = lds_read_tr(qt_ + 16 * ks * D + tofs[1][db]);
-          ov[db] = (u32x4){olo[0], olo[1], ohi[0], ohi[1]};
-          qv[db] = (u32x4){qlo[0], qlo[1], qhi[0], qhi[1]};
+        const u32x4 ovc = ov, qvc = qv;
+        if (i + 1 < 2 * DB) {
+          ov = trf(ot_, i + 1);
+          qv = trf(qt_, i + 1);
         }
+        dv[db] = T::mma(ovc, bp, dv[db]);
+        dk[db] = T::mma(qvc, bd, dk[db]);
         __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int db = 0; db < DB; ++db) {
-          dv[db] = T::mma(ov[db], bp, dv[db]);
-          dk[db] = T::mma(qv[db], bd, dk[db]);
-        }
       }
     }
     __syncthreads();

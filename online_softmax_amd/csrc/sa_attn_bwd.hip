@@ -88,6 +88,7 @@ int sa_attn_bwd(const void* q, const void* k, const void* v, const void* out, co
   st = num_cus(&cus);
   if (st != SA_OK) return st;
   args.pair_ncu = fwd_pair_ncu(B * H_q * args.nqb, args.nqb, causal != 0, 4, cus);
+  args.pair_ncu_kv = fwd_pair_ncu(B * H_kv * args.nkb, args.nkb, causal != 0, 4, cus);
   const bool c = causal != 0, m = key_padding_mask != nullptr, al = alibi_slopes != nullptr;
   hipStream_t hs = (hipStream_t)stream;
   if (dtype == SA_F16) {

@@ -134,3 +134,13 @@ def test_bwd_causal_leak_bitwise():
     dq2, _, _ = run_bwd(inp, dout)
     assert torch.equal(dq1[:, :cut + 1], dq2[:, :cut + 1])
     assert not torch.equal(dq1[:, cut + 1:], dq2[:, cut + 1:])
+
+
+def test_bwd_paired_causal_grid():
+    """A causal grid of exactly two workgroups per CU for both kernels
+    (B * H * 4 blocks of 128 = 512 on a 256-CU device), where workgroups j
+    and j + CUs take complementary blocks of one head; checked in full."""
+    ncu = torch.cuda.get_device_properties(0).multi_processor_count
+    w = Workload("b_pair_grid", 2, 512, 512, 64, 64, 128, "fp16", causal=True, seed=74)
+    print(f"[bwd] {w.B * w.H_q * 4} query blocks and {w.B * w.H_kv * 4} key blocks on {ncu} CUs", flush=True)
+    check(make_inputs(w))
