@@ -46,6 +46,12 @@ CASES = [
     Workload("dec_k32768_256splits", 1, 1, 32768, 4, 1, 128, "bf16", seed=51),
     # Two full head groups of 16 and 300 keys: rounds past the split's end.
     Workload("dec_g32_d128", 2, 1, 300, 32, 1, 128, "fp16", alibi=True, seed=52),
+    # Splits of 2048 keys at D = 64: four rounds of loads per workgroup, the
+    # last split's last round partly past its end.
+    Workload("dec_long_splits", 8, 1, 8000, 16, 8, 64, "bf16", alibi=True, random_tail=2000, seed=64),
+    # Splits of 384 keys at D = 128: two rounds, the second with 4 of its 8
+    # sub-tiles inside the split.
+    Workload("dec_d128_partial_round", 4, 1, 6000, 8, 4, 128, "fp16", random_tail=1500, seed=65),
 ]
 
 
@@ -138,6 +144,10 @@ FUSED_CASES = [
     # two groups of 16 heads at D = 128 over 63 splits: 512 (head, d chunk) pairs,
     # so the merge takes two sweeps of two chunks, the second one ragged
     Workload("fu_b1_g16_d128_40k", 1, 1, 40000, 32, 2, 128, "fp16", decode=True, seed=63),
+    # splits of 2048 and 384 keys (several rounds, the last one partial)
+    Workload("fu_long_splits", 8, 1, 8000, 16, 8, 64, "bf16", decode=True, alibi=True, random_tail=2000,
+             seed=66),
+    Workload("fu_d128_partial_round", 4, 1, 6000, 8, 4, 128, "fp16", decode=True, random_tail=1500, seed=67),
 ]
 
 
