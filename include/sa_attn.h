@@ -130,16 +130,20 @@ int sa_attn_fwd_block_sparse(const void* q, const void* k, const void* v, void* 
  *              As for alibi_slopes, a bias needs a nonzero scale with
  *              1 / |scale| finite (SA_ERR_INVALID_ARG otherwise).
  *   dropout_p  in [0, 1); 0 turns dropout off.  A probability P[i, j] of
- *              (batch b, query head h) is kept when word (j mod 4) of
+ *              (batch b, query head h) is kept when 16-bit half
+ *              (j mod 64) / 32 (0 = low) of word (j mod 4) of
  *              Philox4x32-10 (Salmon et al., SC'11) with counter
- *              (j / 4, i, b * H_q + h, offset) and key (seed low word, seed
- *              high word) is at least floor(dropout_p * 2^32); the output is
+ *              (8 (j / 64) + (j mod 32) / 4, i, b * H_q + h, offset) and key
+ *              (seed low word, seed high word) is at least
+ *              floor(dropout_p * 2^16), so the drop probability is dropout_p
+ *              rounded down to a multiple of 2^-16; the output is
  *              sum_j P[i, j] keep[i, j] v_j / (1 - dropout_p).  lse is that
  *              of the softmax before dropout.
  *   seed, offset: the generator's key and fourth counter word (advance
  *              offset between calls that share a seed).
  *
- * Runs workgroups of four waves.  B == 0 or S_q == 0 is a successful no-op.
+ * Runs workgroups of four waves; with attn_bias NULL and dropout_p 0 the call
+ * is sa_attn_fwd's.  B == 0 or S_q == 0 is a successful no-op.
  * Errors: SA_ERR_INVALID_ARG (also for a dropout_p outside [0, 1), bad bias
  * strides or alignment, out/lse overlapping the bias), SA_ERR_UNSUPPORTED,
  * SA_ERR_HIP.

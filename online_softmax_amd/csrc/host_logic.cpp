@@ -128,8 +128,8 @@ int check_block_sparse(const FwdShape& s, const uint8_t* block_mask, bool* noop)
 }
 
 uint32_t drop_threshold(double p) {
-  const double t = std::floor(p * 4294967296.0);
-  return t >= 4294967295.0 ? 0xFFFFFFFFu : t <= 0.0 ? 0u : (uint32_t)t;
+  const double t = std::floor(p * 65536.0);
+  return t >= 65535.0 ? 0xFFFFu : t <= 0.0 ? 0u : (uint32_t)t;
 }
 
 int check_ext(const FwdShape& s, const ExtShape& e, bool* noop) {

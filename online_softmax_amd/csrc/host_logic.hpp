@@ -81,7 +81,7 @@ struct ExtShape {
 // The forward's checks plus those of the bias (alignment, strides, extent,
 // overlap with out/lse) and of the dropout probability (0 <= p < 1).
 int check_ext(const FwdShape& s, const ExtShape& e, bool* noop);
-// Words below this 32-bit threshold drop: floor(p * 2^32).
+// 16-bit dropout values below this threshold drop: floor(p * 2^16).
 uint32_t drop_threshold(double p);
 
 // The forward's checks plus those of the block mask

@@ -50,8 +50,9 @@
 //    "StreamAttention" page, "Recent Updates"): an additive float32 bias is
 //    loaded for each tile while the previous tile's matrix work runs and is
 //    added to the scores (in accumulator units, like ALiBi) before the
-//    maximum; dropout keeps or zeroes each probability by a Philox4x32-10
-//    word of its (row, key) position, after the row sum has taken it;
+//    maximum; dropout keeps or zeroes each probability by a 16-bit half of a
+//    Philox4x32-10 word of its (row, key) position, after the row sum has
+//    taken it;
 //  * the reference maximum is raised only when a tile's maximum exceeds it by
 //    more than kRescaleSlack (base 2): the final out = numerator / denominator
 //    and lse = reference + log(denominator) are exact for any reference, and
@@ -82,8 +83,9 @@ struct FwdArgs {
   int nkb;                    // key blocks of kSparseBlock per row of block_mask
   // Extended mode.  Bias element (b, h, i, j) at bias[b sb + h sh + i sq + j]
   // (strides in elements, multiples of 4; NULL = none).  Dropout: a
-  // probability is kept when its Philox word is >= drop_thr (0 = no dropout);
-  // kept ones are scaled by drop_scale = 1 / (1 - p) in the epilogue.
+  // probability is kept when its 16-bit Philox value is >= drop_thr (0 = no
+  // generator calls: every value is); the output is scaled by drop_scale =
+  // 1 / (1 - p) in the epilogue (1 without dropout).
   const float* bias;
   int64_t bias_sb, bias_sh, bias_sq;
   uint32_t drop_thr;
@@ -545,17 +547,24 @@ __global__ __launch_bounds__(NW * 64, EXT ? 1 : 2) void fwd_kernel(FwdArgs a) {
       for (int e = 0; e < 4; ++e) s[u >> 2][4 * (u & 3) + e] = fmaf(bv[u][e], a.alibi2, s[u >> 2][4 * (u & 3) + e]);
   };
   // Dropout keep bits of the tile of iteration it: bit 16 jb + r for register
-  // r of block jb.  One generator block per quarter of four keys, counter
-  // (key / 4, row, b * H_q + h, offset), word key % 4.
+  // r of block jb.  Key j is decided by 16-bit half (j mod 64) / 32 of word
+  // j mod 4 of the generator block with counter (8 (j / 64) + (j mod 32) / 4,
+  // row, b * H_q + h, offset).  A tile is one 64-key window, and the lane's
+  // keys 32 jb + 8 u + 4 g + e of it (register 4 u + e of block jb) take
+  // half jb of word e of block 8 (n0 / 64) + 2 u + g: four blocks per tile.
+  static_assert(BN == 64, "the dropout counters assume 64-key tiles");
   auto keep_bits = [&](const int it) __attribute__((always_inline)) -> uint32_t {
     const int n0 = wtile(it) * BN;
+    const uint32_t c0 = (uint32_t)(n0 >> 3) + (uint32_t)g;
     uint32_t bits = 0;
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const int j0 = n0 + 32 * (u >> 2) + 8 * (u & 3) + 4 * g;
-      const u32x4 wd = philox4x32_10((uint32_t)(j0 >> 2), plane);
+    for (int u = 0; u < 4; ++u) {
+      const u32x4 wd = philox4x32_10(c0 + 2u * (uint32_t)u, plane);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) bits |= (wd[e] >= a.drop_thr ? 1u : 0u) << (16 * (u >> 2) + 4 * (u & 3) + e);
+      for (int e = 0; e < 4; ++e) {
+        bits |= ((wd[e] & 0xFFFFu) >= a.drop_thr ? 1u : 0u) << (4 * u + e);
+        bits |= ((wd[e] >> 16) >= a.drop_thr ? 1u : 0u) << (16 + 4 * u + e);
+      }
     }
     return bits;
   };
@@ -919,7 +928,7 @@ __global__ __launch_bounds__(NW * 64, EXT ? 1 : 2) void fwd_kernel(FwdArgs a) {
   const float l_tot = sum_halves(l_run);
   if (qvalid && gw == 0) {
     float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-    if (dropping) inv *= a.drop_scale;
+    if constexpr (EXT) inv *= a.drop_scale;
     uint16_t* op = a.out + ((size_t)(b * (size_t)a.S_q + qi) * a.H_q + h) * D + 4 * g;
 #pragma unroll
     for (int db = 0; db < DB; ++db) {

@@ -4,7 +4,8 @@
 // additive float bias and Philox dropout): validate (host_logic.cpp, no HIP
 // call), pick the template instance for {dtype, D, causal, mask, ALiBi},
 // launch workgroups of four waves (the bias registers leave no room for the
-// eight-wave layout) on the caller's stream.
+// eight-wave layout) on the caller's stream.  Without a bias and without
+// dropout the call is the plain forward's.
 #include <hip/hip_runtime.h>
 
 #include <cmath>
@@ -56,6 +57,10 @@ int sa_attn_fwd_ext(const void* q, const void* k, const void* v, void* out, floa
   bool noop = false;
   int st = check_ext(shp, ext, &noop);
   if (st != SA_OK || noop) return st;
+  // Neither a bias nor dropout: the plain forward computes exactly this.
+  if (attn_bias == nullptr && dropout_p == 0.0)
+    return sa_attn_fwd(q, k, v, out, lse, B, S_q, S_k, H_q, H_kv, D, scale, causal, key_padding_mask,
+                       alibi_slopes, dtype, stream);
 
   FwdArgs args;
   args.q = (const uint16_t*)q;

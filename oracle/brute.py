@@ -23,9 +23,9 @@ def attention(q, k, v, scale, causal=False, key_padding_mask=None,
     selected) restricts row i to keys whose block of ``block`` keys is
     selected for the block of ``block`` rows holding i.  ``attn_bias``
     (nested ``[B][H_q][S_q][S_k]``) is added to the scaled score; with
-    ``dropout_p > 0`` each term of the output sum is kept when its Philox word
-    (one generator call per element) reaches the drop threshold, and is then
-    divided by ``1 - dropout_p``.
+    ``dropout_p > 0`` each term of the output sum is kept when its 16-bit
+    Philox value (one generator call per element) reaches the drop
+    threshold, and is then divided by ``1 - dropout_p``.
 
     Returns ``(out [B][S_q][H_q][D], lse [B][H_q][S_q])`` as Python floats.
     """
@@ -68,9 +68,11 @@ def attention(q, k, v, scale, causal=False, key_padding_mask=None,
                 if dropout_p > 0.0:
                     thr = drop_threshold(dropout_p)
                     for n, j in enumerate(keys):
-                        word = philox4x32_10((j // 4, i, b * H_q + h, offset),
-                                             (seed & 0xFFFFFFFF, seed >> 32))[j % 4]
-                        weight[n] = weight[n] / (1.0 - dropout_p) if word >= thr else 0.0
+                        window, within = divmod(j, 64)
+                        word = philox4x32_10((8 * window + (within % 32) // 4, i, b * H_q + h, offset),
+                                             (seed & 0xFFFFFFFF, seed >> 32))[within % 4]
+                        value = (word >> 16) if within >= 32 else (word & 0xFFFF)
+                        weight[n] = weight[n] / (1.0 - dropout_p) if value >= thr else 0.0
                 for d in range(D):
                     out[b][i][h][d] = math.fsum(
                         wt * float(v[b][j][hk][d]) for wt, j in zip(weight, keys))

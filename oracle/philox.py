@@ -9,11 +9,16 @@ products; the new counter is (hi(M1 c2) ^ c1 ^ k0, lo(M1 c2), hi(M0 c0) ^ c3
 constants.  The multipliers and Weyl constants are the published ones.
 
 The dropout rule built on it (the "StreamAttention" page names deterministic
-Philox seeding for dropout in "Recent Updates"; the counter layout is a
-reading of this repository): the probability of query row i, key j in
-(batch b, head h) is kept when word ``j % 4`` of
-``philox((j // 4, i, b * H_q + h, offset), (seed_lo, seed_hi))`` is at least
-``drop_threshold(p)``.
+Philox seeding for dropout in "Recent Updates"; the counter layout and the
+16-bit decisions are a reading of this repository): each generator block
+gives eight 16-bit values, one per decision.  The probability of query row
+i, key j in (batch b, head h) is decided by 16-bit half ``(j % 64) // 32``
+(0 = low, 1 = high) of word ``j % 4`` of the block with counter
+``(8 (j // 64) + (j % 32) // 4, i, b * H_q + h, offset)`` and key
+``(seed_lo, seed_hi)``: within each window of 64 keys, keys j and j + 32
+share a word.  It is kept when that value is at least ``drop_threshold(p)``
+= floor(p 2^16), so the drop probability is p rounded down to a multiple of
+2^-16.
 
 ``philox4x32_10`` works on Python ints one block at a time; ``philox_words``
 is the same arithmetic vectorised over numpy uint64 arrays.
@@ -61,17 +66,29 @@ def philox_words(c0, c1, c2, c3, k0, k1):
 
 
 def drop_threshold(p):
-    """Words below this 32-bit threshold drop: floor(p * 2^32), for 0 <= p < 1."""
+    """16-bit values below this threshold drop: floor(p * 2^16), for 0 <= p < 1."""
     if not 0.0 <= p < 1.0:
         raise ValueError("dropout probability must be in [0, 1)")
-    return min(int(math.floor(float(p) * 2.0 ** 32)), MASK32)
+    return min(int(math.floor(float(p) * 2.0 ** 16)), 0xFFFF)
+
+
+def decision_slot(j):
+    """(block counter word c0, word, half) of key j's decision."""
+    return 8 * (j // 64) + (j % 32) // 4, j % 4, (j % 64) // 32
+
+
+def dropout_values(b, h, H_q, rows, S_k, seed, offset=0):
+    """The 16-bit decision values ``[R, S_k]`` (uint64) of (batch b, head h)
+    for query rows ``rows``."""
+    rows = np.asarray(rows, dtype=np.int64)
+    j = np.arange(S_k, dtype=np.int64)
+    c0, word, half = decision_slot(j)
+    words = philox_words(c0[None, :], rows[:, None], b * H_q + h, offset,
+                         seed & MASK32, (seed >> 32) & MASK32)
+    w = np.choose(word[None, :].repeat(len(rows), axis=0), words)
+    return (w >> (np.uint64(16) * half.astype(np.uint64))[None, :]) & np.uint64(0xFFFF)
 
 
 def keep_mask(b, h, H_q, rows, S_k, p, seed, offset=0):
     """Boolean ``[R, S_k]`` keep decisions of (batch b, head h) for query rows ``rows``."""
-    rows = np.asarray(rows, dtype=np.int64)
-    j = np.arange(S_k, dtype=np.int64)
-    words = philox_words((j // 4)[None, :], rows[:, None], b * H_q + h, offset,
-                         seed & MASK32, (seed >> 32) & MASK32)
-    w = np.choose((j % 4)[None, :].repeat(len(rows), axis=0), words)
-    return w >= np.uint64(drop_threshold(p))
+    return dropout_values(b, h, H_q, rows, S_k, seed, offset) >= np.uint64(drop_threshold(p))

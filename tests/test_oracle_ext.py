@@ -148,13 +148,31 @@ def pin_plain_without_extras(fn):
 
 
 def pin_brute_dropout(fn):
-    for n, (p, seed, offset) in enumerate([(0.3, 1234567, 0), (0.5, 2 ** 40 + 99, 7), (0.1, 3, 1)]):
-        q, k, v, sc, c, m, sl, bias = make(30 + n, B=2, S_q=5, S_k=10, H_q=2, H_kv=1, D=3)
+    # The last case spans three 64-key windows: both halves of the words and
+    # several block counters per row.
+    for n, (p, seed, offset, S_k) in enumerate([(0.3, 1234567, 0, 10), (0.5, 2 ** 40 + 99, 7, 10),
+                                                 (0.1, 3, 1, 10), (0.4, 2 ** 63 + 5, 3, 150)]):
+        q, k, v, sc, c, m, sl, bias = make(30 + n, B=2, S_q=5 if S_k < 64 else 2, S_k=S_k, H_q=2, H_kv=1, D=3)
+        S_q = q.shape[1]
         o, l = fn(q, k, v, sc, c, m, sl, attn_bias=bias, dropout_p=p, seed=seed, offset=offset)
         bo, bl = brute.attention(q.tolist(), k.tolist(), v.tolist(), sc, c, m.tolist(), sl.tolist(),
-                                 attn_bias=np.broadcast_to(bias, (2, 2, 5, 10)).tolist(),
+                                 attn_bias=np.broadcast_to(bias, (2, 2, S_q, S_k)).tolist(),
                                  dropout_p=p, seed=seed, offset=offset)
         assert close(o, np.array(bo)) and close(l, np.array(bl)), (p, seed)
+
+
+def pin_dropout_uses_each_half_once(fn):
+    """Over whole 64-key windows a row's decisions use every 16-bit half of
+    the row's blocks exactly once: the values of keys 0 .. 191 are, as a
+    multiset, the 24 blocks' 192 halves (computed here block by block)."""
+    seed, offset, H_q, b, h = 0x0123456789ABCDEF, 9, 3, 1, 2
+    for row in (0, 5):
+        vals = philox.dropout_values(b, h, H_q, [row], 192, seed, offset)[0]
+        halves = []
+        for c0 in range(24):
+            for w in philox.philox4x32_10((c0, row, b * H_q + h, offset), (seed & 0xFFFFFFFF, seed >> 32)):
+                halves += [w & 0xFFFF, w >> 16]
+        assert sorted(int(x) for x in vals) == sorted(halves)
 
 
 def pin_dropout_statistics(fn):
@@ -180,7 +198,7 @@ def pin_dropout_statistics(fn):
 
 
 PINS = [pin_bias_sdpa, pin_ninf_bias_is_mask, pin_plain_without_extras, pin_brute_dropout,
-        pin_dropout_statistics]
+        pin_dropout_statistics, pin_dropout_uses_each_half_once]
 GEN_PINS = [pin_philox_kat, pin_philox_vectorised]
 
 
@@ -200,8 +218,9 @@ def test_philox_pins(pin):
 
 def test_threshold_and_validation():
     assert philox.drop_threshold(0.0) == 0
-    assert philox.drop_threshold(0.5) == 2 ** 31
-    assert philox.drop_threshold(1 - 2 ** -40) == 2 ** 32 - 1
+    assert philox.drop_threshold(0.5) == 2 ** 15
+    assert philox.drop_threshold(0.1) == 6553
+    assert philox.drop_threshold(1 - 2 ** -40) == 2 ** 16 - 1
     for bad in (-0.1, 1.0, 1.5):
         with pytest.raises(ValueError):
             philox.drop_threshold(bad)
@@ -228,8 +247,19 @@ def _swapped_keep(b, h, H_q, rows, S_k, p, seed, offset=0):
     j = np.arange(S_k, dtype=np.int64)
     words = philox.philox_words(rows[:, None] // 4, j[None, :], b * H_q + h, offset,
                                 seed & 0xFFFFFFFF, seed >> 32)
-    w = np.choose((rows % 4)[:, None].repeat(S_k, axis=1), words)
+    w = np.choose((rows % 4)[:, None].repeat(S_k, axis=1), words) & np.uint64(0xFFFF)
     return w >= np.uint64(philox.drop_threshold(p))
+
+
+def _halves_swapped(b, h, H_q, rows, S_k, p, seed, offset=0):
+    rows = np.asarray(rows, dtype=np.int64)
+    j = np.arange(S_k, dtype=np.int64)
+    c0, word, half = philox.decision_slot(j)
+    words = philox.philox_words(c0[None, :], rows[:, None], b * H_q + h, offset,
+                                seed & 0xFFFFFFFF, seed >> 32)
+    w = np.choose(word[None, :].repeat(len(rows), axis=0), words)
+    v = (w >> (np.uint64(16) * (1 - half).astype(np.uint64))[None, :]) & np.uint64(0xFFFF)
+    return v >= np.uint64(philox.drop_threshold(p))
 
 
 def _wrap(transform):
@@ -244,6 +274,7 @@ MUTANTS = {
     "dropout keeps the words below the threshold": _Patched(philox, "keep_mask", lambda f: (
         lambda b, h, H, rows, S_k, p, seed, offset=0: ~f(b, h, H, rows, S_k, p, seed, offset))),
     "dropout counter with row and key swapped": _Patched(philox, "keep_mask", lambda f: _swapped_keep),
+    "dropout word halves swapped": _Patched(philox, "keep_mask", lambda f: _halves_swapped),
     "bias sign flipped": _wrap(lambda q, k, v, sc, c, m, sl, **kw: call_ext(
         q, k, v, sc, c, m, sl, **{**kw, "attn_bias": None if kw.get("attn_bias") is None else -kw["attn_bias"]})),
     "bias added before the scale": _wrap(lambda q, k, v, sc, c, m, sl, **kw: call_ext(
