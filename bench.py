@@ -445,6 +445,30 @@ def copy_calibration(args, dev):
                       "read_plus_write_GBs": round(2 * n / dt / 1e9, 1)}), flush=True)
 
 
+def gemm_calibration(args, dev):
+    """A plain bfloat16 matrix product (torch.matmul, n x n x n) for a
+    reference of what the matrix cores sustain on this GPU outside attention."""
+    import torch
+    n = args.gemm
+    a = torch.randn(n, n, device=dev).to(torch.bfloat16)
+    b = torch.randn(n, n, device=dev).to(torch.bfloat16)
+    c = torch.empty(n, n, device=dev, dtype=torch.bfloat16)
+    for _ in range(args.warmup):
+        torch.matmul(a, b, out=c)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(args.steps):
+        torch.matmul(a, b, out=c)
+    e1.record()
+    torch.cuda.synchronize()
+    dt = e0.elapsed_time(e1) / 1e3 / args.steps
+    flops = 2.0 * n ** 3
+    print(json.dumps({"gemm_n": n, "dtype": "bf16", "ms_per_gemm": round(dt * 1e3, 4),
+                      "TFLOPs": round(flops / dt / 1e12, 1),
+                      "frac_of_2500": round(flops / dt / 1e12 / MFMA_PEAK_TFLOPS, 4)}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -458,6 +482,8 @@ def main():
     ap.add_argument("--cpu-table", action="store_true",
                     help="instead of the hot path, print the float64 oracle's wall time per configuration "
                          "on this host (all BLAS threads, and one thread for configurations 1, 2 and 4)")
+    ap.add_argument("--gemm", type=int, default=0,
+                    help="instead of the hot path, time a plain n x n x n bfloat16 torch.matmul")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="instead of the hot path, time a plain device-to-device copy of this many "
                          "MiB (the reference kernel for scaling HBM byte counters)")
@@ -469,8 +495,8 @@ def main():
         print(json.dumps(cpu_table()), flush=True)
         return
     if args.gpus != 1:
-        print(f"bench.py runs on exactly one GPU (asked for {args.gpus}); multi-GPU sharding is "
-              "not part of this build.", file=sys.stderr)
+        print(f"bench.py runs on exactly one GPU (asked for {args.gpus}); the library has no "
+              "multi-GPU path.", file=sys.stderr)
         sys.exit(2)
 
     import torch
@@ -478,6 +504,9 @@ def main():
     dev = torch.device("cuda:0")
     if args.copy_mib:
         copy_calibration(args, dev)
+        return
+    if args.gemm:
+        gemm_calibration(args, dev)
         return
     parts = [Part(n, dev) for n in STEPS[args.workload]]
     stream = torch.cuda.current_stream(dev)
