@@ -194,6 +194,12 @@ int fwd_pair_ncu(int nitems, int nmb, bool causal, int nw, int num_cu) {
   return (int64_t)nitems == 2 * (int64_t)num_cu ? num_cu : 0;
 }
 
+int fwd_persistent_grid(int bh, int nmb, bool causal, int nw, int num_cu) {
+  if (num_cu <= 0 || bh <= 0 || nmb <= 0 || !(nw == 8 || causal)) return 0;
+  const int64_t units = (int64_t)bh * (causal ? (nmb + 1) / 2 : nmb);
+  return units >= 2 * (int64_t)num_cu ? num_cu : 0;
+}
+
 int decode_chunk(int S_k, int splits) {
   if (splits < 1) splits = 1;
   int per = (S_k + splits - 1) / splits;

@@ -105,6 +105,13 @@ int fwd_waves(int B, int S_q, int H_q, bool causal, int num_cu);
 // (two resident per CU) has exactly two workgroups per CU and an even number
 // of blocks per head, else 0.
 int fwd_pair_ncu(int nitems, int nmb, bool causal, int nw, int num_cu);
+// The grid of the forward's persistent schedule (one eight-wave workgroup
+// per CU working through units of one (batch, head) and a complementary pair
+// of causal blocks, or one block without the causal rule), or 0 for one
+// block per workgroup.  Used for the eight-wave kernels (nw = 8, or causal
+// with nw = 4, which runs eight waves in two groups) when there are at least
+// two units per CU.
+int fwd_persistent_grid(int bh, int nmb, bool causal, int nw, int num_cu);
 // Keys per split for a split count (a multiple of kDecodeStepKeys).
 int decode_chunk(int S_k, int splits);
 size_t decode_workspace_size(int B, int H_q, int S_k, int D);

@@ -169,10 +169,31 @@ __device__ inline int lds_swizzle(int r) {
 // state joins group 0's at the end.  Eight waves then cover a 128-row block
 // at two waves per SIMD, so that causal blocks of very unequal length can be
 // spread over the CUs heaviest first instead of pairing them on one CU.
+// The persistent schedule (PERSIST): the grid holds one workgroup per CU,
+// and each works through units of its XCD's share, a unit being one (batch,
+// head) and a pair of causal blocks x and nmb - 1 - x (the heavier first) --
+// so that every unit carries the same work -- or one block without the
+// causal rule.  The XCDs (workgroups are dealt to them round-robin) own
+// contiguous ranges of units and their workgroups take the units in turn, so
+// the units of one (batch, head) run at the same time on one L2.
+template <bool CAUSAL>
+__device__ inline int persist_upb(const FwdArgs& a) { return CAUSAL ? (a.nmb + 1) / 2 : a.nmb; }
+template <bool CAUSAL>
+__device__ inline int2 persist_range(const FwdArgs& a) {
+  const int nunits = a.nitems / a.nmb * persist_upb<CAUSAL>(a);
+  const int x = blockIdx.x & 7;
+  const int u0 = x * (nunits >> 3) + min(x, nunits & 7);
+  return make_int2(u0, u0 + (nunits >> 3) + (x < (nunits & 7) ? 1 : 0));
+}
+__device__ inline int persist_stride() {
+  return ((int)gridDim.x >> 3) + ((int)(blockIdx.x & 7) < ((int)gridDim.x & 7) ? 1 : 0);
+}
+
 template <class T, int D, bool CAUSAL, bool MASK, bool ALIBI, int NW, bool SPARSE = false,
-          bool EXT = false, int NG = 1>
+          bool EXT = false, int NG = 1, bool PERSIST = false>
 __global__ __launch_bounds__(NW * 64, EXT ? 1 : 2) void fwd_kernel(FwdArgs a) {
   static_assert(NG == 1 || (NG == 2 && NW == 8 && !SPARSE && !EXT), "two groups: dense eight-wave kernel only");
+  static_assert(!PERSIST || (!SPARSE && !EXT), "persistent schedule: dense kernels only");
   constexpr int NWG = NW / NG;       // waves per group
   constexpr int BM = 32 * NWG;       // query rows per workgroup
   constexpr int BN = 64;             // keys per tile
@@ -190,18 +211,39 @@ __global__ __launch_bounds__(NW * 64, EXT ? 1 : 2) void fwd_kernel(FwdArgs a) {
   __shared__ int Lw[MASK ? NW : 1];  // per-wave last kept key
   __shared__ int16_t Tl[SPARSE ? kSparseMaxTiles : 1];  // block-sparse tile list
   __shared__ int Tn;                                     // its length
+  // Persistent schedule: the current unit and which of its blocks (kept in
+  // LDS rather than in registers across the sweep).
+  __shared__ int s_unit[2];
 
+  if constexpr (PERSIST) {
+    if (threadIdx.x == 0) {
+      s_unit[0] = persist_range<CAUSAL>(a).x + (int)(blockIdx.x >> 3);
+      s_unit[1] = 0;
+    }
+    __syncthreads();
+  }
+  for (;;) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int li = lane & 31, g = lane >> 5;
   const int gw = NG == 1 ? 0 : w / NWG;  // this wave's group
   const int wi = w - gw * NWG;           // and its place in the group
-
-  const int item = xcd_contiguous(blockIdx.x, a.nitems);
-  const int bh = item / a.nmb;
-  const int mbi = item - bh * a.nmb;
-  // Causal blocks are issued heaviest (last rows) first.
-  const int mb = CAUSAL ? a.nmb - 1 - mbi : mbi;
+  int bh, mb;
+  if constexpr (!PERSIST) {
+    const int item = xcd_contiguous(blockIdx.x, a.nitems);
+    bh = item / a.nmb;
+    const int mbi = item - bh * a.nmb;
+    // Causal blocks are issued heaviest (last rows) first.
+    mb = CAUSAL ? a.nmb - 1 - mbi : mbi;
+  } else {
+    const int q = __builtin_amdgcn_readfirstlane(s_unit[0]);
+    const int half = __builtin_amdgcn_readfirstlane(s_unit[1]);
+    if (q >= persist_range<CAUSAL>(a).y) break;
+    const int upb = persist_upb<CAUSAL>(a);
+    bh = q / upb;
+    const int x = q - bh * upb;
+    mb = CAUSAL && half == 0 ? a.nmb - 1 - x : x;
+  }
   const int b = bh / a.H_q, h = bh - b * a.H_q, hk = h / a.G;
   const int m0 = mb * BM;
   const int off = a.S_k - a.S_q;  // bottom-right alignment of the causal rule
@@ -840,6 +882,10 @@ __global__ __launch_bounds__(NW * 64, EXT ? 1 : 2) void fwd_kernel(FwdArgs a) {
   };
 
   wait_vmem();
+  // Persistent schedule: no scalar load is left in flight into the sweep
+  // (the per-block reloads of kernel arguments), so that the waits for the
+  // sweep's LDS reads can count them exactly.
+  if constexpr (PERSIST) __builtin_amdgcn_s_waitcnt(0xc07f);
   __syncthreads();
 
   f32x16 sa[2], sb[2];
@@ -941,6 +987,26 @@ __global__ __launch_bounds__(NW * 64, EXT ? 1 : 2) void fwd_kernel(FwdArgs a) {
     }
     if (g == 0 && a.lse)
       a.lse[((size_t)b * a.H_q + h) * a.S_q + qi] = l_tot > 0.f ? (m_ref + __log2f(l_tot)) * kLn2 : kNegInf;
+  }
+  if constexpr (!PERSIST) {
+    break;
+  } else {
+    // Every wave has read the unit and is done with the buffers (the next
+    // block's copies reuse them, after the two-group hand-over too); then the
+    // next unit or block.
+    __syncthreads();
+    if (tid == 0) {
+      const int q = s_unit[0], upb = persist_upb<CAUSAL>(a);
+      const int x = q % upb;
+      if (CAUSAL && s_unit[1] == 0 && x < a.nmb - 1 - x) {
+        s_unit[1] = 1;
+      } else {
+        s_unit[0] = q + persist_stride();
+        s_unit[1] = 0;
+      }
+    }
+    __syncthreads();
+  }
   }
 }
 

@@ -24,27 +24,34 @@ namespace {
 // 17.0-17.3 us (with ALiBi 19.7 -> 18.5 us), [1,8192,8,128] causal ALiBi with
 // padding 169-174 -> 154-160 us.
 template <class T, int D, bool C, bool M, bool A>
-void launch_fwd(const FwdArgs& args, int nw, hipStream_t st) {
-  if (nw == 8)
-    hipLaunchKernelGGL((fwd_kernel<T, D, C, M, A, 8>), dim3(args.nitems), dim3(512), 0, st, args);
-  else if constexpr (C)
-    hipLaunchKernelGGL((fwd_kernel<T, D, C, M, A, 8, false, false, 2>), dim3(args.nitems), dim3(512), 0, st, args);
-  else
+void launch_fwd(const FwdArgs& args, int nw, int pgrid, hipStream_t st) {
+  if (nw == 8) {
+    if (pgrid > 0)
+      hipLaunchKernelGGL((fwd_kernel<T, D, C, M, A, 8, false, false, 1, true>), dim3(pgrid), dim3(512), 0, st, args);
+    else
+      hipLaunchKernelGGL((fwd_kernel<T, D, C, M, A, 8>), dim3(args.nitems), dim3(512), 0, st, args);
+  } else if constexpr (C) {
+    if (pgrid > 0)
+      hipLaunchKernelGGL((fwd_kernel<T, D, C, M, A, 8, false, false, 2, true>), dim3(pgrid), dim3(512), 0, st, args);
+    else
+      hipLaunchKernelGGL((fwd_kernel<T, D, C, M, A, 8, false, false, 2>), dim3(args.nitems), dim3(512), 0, st, args);
+  } else {
     hipLaunchKernelGGL((fwd_kernel<T, D, C, M, A, 4>), dim3(args.nitems), dim3(256), 0, st, args);
+  }
 }
 
 template <class T, int D>
-void dispatch_fwd(const FwdArgs& args, bool causal, bool mask, bool alibi, int nw, hipStream_t st) {
+void dispatch_fwd(const FwdArgs& args, bool causal, bool mask, bool alibi, int nw, int grid, hipStream_t st) {
   const int key = (causal ? 4 : 0) | (mask ? 2 : 0) | (alibi ? 1 : 0);
   switch (key) {
-    case 0: launch_fwd<T, D, false, false, false>(args, nw, st); break;
-    case 1: launch_fwd<T, D, false, false, true>(args, nw, st); break;
-    case 2: launch_fwd<T, D, false, true, false>(args, nw, st); break;
-    case 3: launch_fwd<T, D, false, true, true>(args, nw, st); break;
-    case 4: launch_fwd<T, D, true, false, false>(args, nw, st); break;
-    case 5: launch_fwd<T, D, true, false, true>(args, nw, st); break;
-    case 6: launch_fwd<T, D, true, true, false>(args, nw, st); break;
-    default: launch_fwd<T, D, true, true, true>(args, nw, st); break;
+    case 0: launch_fwd<T, D, false, false, false>(args, nw, grid, st); break;
+    case 1: launch_fwd<T, D, false, false, true>(args, nw, grid, st); break;
+    case 2: launch_fwd<T, D, false, true, false>(args, nw, grid, st); break;
+    case 3: launch_fwd<T, D, false, true, true>(args, nw, grid, st); break;
+    case 4: launch_fwd<T, D, true, false, false>(args, nw, grid, st); break;
+    case 5: launch_fwd<T, D, true, false, true>(args, nw, grid, st); break;
+    case 6: launch_fwd<T, D, true, true, false>(args, nw, grid, st); break;
+    default: launch_fwd<T, D, true, true, true>(args, nw, grid, st); break;
   }
 }
 
@@ -159,14 +166,15 @@ int sa_attn_fwd(const void* q, const void* k, const void* v, void* out, float* l
   args.nitems = B * H_q * args.nmb;
   args.block_mask = nullptr;
   args.nkb = 0;
+  const int grid = fwd_persistent_grid(B * H_q, args.nmb, causal != 0, nw, cus);
   const bool c = causal != 0, m = key_padding_mask != nullptr, al = alibi_slopes != nullptr;
   hipStream_t hs = (hipStream_t)stream;
   if (dtype == SA_F16) {
-    if (D == 64) dispatch_fwd<F16, 64>(args, c, m, al, nw, hs);
-    else dispatch_fwd<F16, 128>(args, c, m, al, nw, hs);
+    if (D == 64) dispatch_fwd<F16, 64>(args, c, m, al, nw, grid, hs);
+    else dispatch_fwd<F16, 128>(args, c, m, al, nw, grid, hs);
   } else {
-    if (D == 64) dispatch_fwd<BF16, 64>(args, c, m, al, nw, hs);
-    else dispatch_fwd<BF16, 128>(args, c, m, al, nw, hs);
+    if (D == 64) dispatch_fwd<BF16, 64>(args, c, m, al, nw, grid, hs);
+    else dispatch_fwd<BF16, 128>(args, c, m, al, nw, grid, hs);
   }
   return launched("attention forward");
 }

@@ -303,6 +303,61 @@ EIGHT_WAVE = [
 ]
 
 
+def _persistent_units(w):
+    """Units of the forward's persistent schedule for this shape (a causal
+    unit pairs two query blocks) and whether it takes it: eight-wave
+    workgroups (256-row blocks, or 128-row blocks in two groups under the
+    causal rule) and at least two units per CU."""
+    ncu = torch.cuda.get_device_properties(0).multi_processor_count
+    nw = 8 if _eight_wave(w) else 4
+    if nw == 4 and not w.causal:
+        return 0, False
+    nmb = -(-w.S_q // (32 * nw))
+    units = w.B * w.H_q * (-(-nmb // 2) if w.causal else nmb)
+    return units, units >= 2 * ncu
+
+
+PERSISTENT = [
+    # 256-row blocks without the causal rule: 512 units of one block
+    Workload("persist_plain_f16_d64", 2, 300, 300, 128, 16, 64, "fp16", seed=160),
+    # 128-row blocks in two groups, five per head: units of blocks 4 and 0,
+    # 3 and 1, and block 2 alone
+    Workload("persist_groups_odd_f16_d64", 4, 640, 640, 64, 16, 64, "fp16", causal=True, random_tail=100,
+             seed=161),
+    Workload("persist_groups_alibi_bf16_d64", 4, 600, 640, 64, 8, 64, "bf16", causal=True, alibi=True, seed=162),
+]
+
+
+@pytest.mark.parametrize("w", PERSISTENT, ids=lambda w: w.name)
+def test_persistent_schedule_full(w):
+    """Shapes with at least two units per CU, where each workgroup of the
+    forward works through a list of (batch, head, block pair) units: checked
+    in full against the oracle."""
+    units, persistent = _persistent_units(w)
+    print(f"[fwd] {w.name}: {units} units, persistent schedule: {persistent}", flush=True)
+    if not persistent:
+        pytest.skip("this device has too many compute units for the shape to take the persistent schedule")
+    check(make_inputs(w), what=w.name)
+
+
+def test_persistent_schedule_ragged_units_sampled():
+    """600 units (eight-wave causal pairs; 150 heads of 1800 rows) spread
+    unevenly over the XCDs and CUs: sampled rows, and every row written."""
+    w = Workload("persist_ragged_units", 3, 1800, 1800, 50, 10, 64, "fp16", causal=True, random_tail=200, seed=163)
+    units, persistent = _persistent_units(w)
+    print(f"[fwd] {w.name}: {units} units, persistent schedule: {persistent}", flush=True)
+    if not persistent:
+        pytest.skip("this device has too many compute units for the shape to take the persistent schedule")
+    inp = make_inputs(w)
+    out, lse = check(inp, rows=_sample_rows(w.S_q, 16, 7), what=w.name)
+    q, k, v, m, s = to_dev(inp)
+    o2 = torch.full_like(q, float("nan"))
+    l2 = torch.full((w.B, w.H_q, w.S_q), float("nan"), dtype=torch.float32, device="cuda")
+    sa.attn_fwd(q, k, v, causal=True, scale=w.scale, key_padding_mask=m, out=o2, lse=l2)
+    torch.cuda.synchronize()
+    assert not torch.isnan(o2).any() and not torch.isnan(l2).any()
+
+
 @pytest.mark.parametrize("w", EIGHT_WAVE, ids=lambda w: w.name)
 def test_eight_wave_full(w):
     """Grids large enough for the 256-row eight-wave workgroups, checked in
