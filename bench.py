@@ -20,7 +20,7 @@ event between the parts of a step.  Each part is then timed on its own: K
 calls back to back between two events, after the warm-up count of calls
 (and, for a part shorter on the device than its host launch, the decode, a
 lead of matrix multiplies so that the device never waits for the host).
-Ahead of the warm-up and timed steps bench.py queues at least 40 ms of
+Ahead of the warm-up and timed steps bench.py queues at least 150 ms of
 4096^3 fp16 matrix multiplies, so that the device never waits for the host
 and the timed steps run at the clock sustained work holds, not in the ramp
 that follows an idle gap.
@@ -70,7 +70,7 @@ HBM_PEAK_GBS = 8000.0       # MI355X HBM3E bandwidth (published)
 # bytes (three times the 256 MB last-level cache), and at least 8 copies.
 DECODE_ROTATION_BYTES = 768 << 20
 # Least device time of the matrix-multiply lead queued ahead of the timed steps.
-PREHEAT_MS = 40.0
+PREHEAT_MS = 150.0
 PROFILES = ROOT / "profiles"
 # Sources each kernel is built from: a traffic figure measured on other sources is stale.
 # Each mode of an entry point has its own kernel instances and so its own
