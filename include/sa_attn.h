@@ -142,8 +142,9 @@ int sa_attn_fwd_block_sparse(const void* q, const void* k, const void* v, void* 
  *   seed, offset: the generator's key and fourth counter word (advance
  *              offset between calls that share a seed).
  *
- * Runs workgroups of four waves; with attn_bias NULL and dropout_p 0 the call
- * is sa_attn_fwd's.  B == 0 or S_q == 0 is a successful no-op.
+ * Runs workgroups of four waves, or with dropout under the causal rule and
+ * without ALiBi eight waves in two groups; with attn_bias NULL and dropout_p
+ * 0 the call is sa_attn_fwd's.  B == 0 or S_q == 0 is a successful no-op.
  * Errors: SA_ERR_INVALID_ARG (also for a dropout_p outside [0, 1), bad bias
  * strides or alignment, out/lse overlapping the bias), SA_ERR_UNSUPPORTED,
  * SA_ERR_HIP.

@@ -191,8 +191,8 @@ __device__ inline int persist_stride() {
 
 template <class T, int D, bool CAUSAL, bool MASK, bool ALIBI, int NW, bool SPARSE = false,
           bool EXT = false, int NG = 1, bool PERSIST = false>
-__global__ __launch_bounds__(NW * 64, EXT ? 1 : 2) void fwd_kernel(FwdArgs a) {
-  static_assert(NG == 1 || (NG == 2 && NW == 8 && !SPARSE && !EXT), "two groups: dense eight-wave kernel only");
+__global__ __launch_bounds__(NW * 64, EXT && NG == 1 ? 1 : 2) void fwd_kernel(FwdArgs a) {
+  static_assert(NG == 1 || (NG == 2 && NW == 8 && !SPARSE && !(EXT && ALIBI)), "two groups: dense eight-wave kernel only");
   static_assert(!PERSIST || (!SPARSE && !EXT), "persistent schedule: dense kernels only");
   constexpr int NWG = NW / NG;       // waves per group
   constexpr int BM = 32 * NWG;       // query rows per workgroup

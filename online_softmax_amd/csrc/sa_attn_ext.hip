@@ -3,9 +3,15 @@
 // Host code around the extended mode of the prefill kernel (prefill.hpp:
 // additive float bias and Philox dropout): validate (host_logic.cpp, no HIP
 // call), pick the template instance for {dtype, D, causal, mask, ALiBi},
-// launch workgroups of four waves (the bias registers leave no room for the
-// eight-wave layout) on the caller's stream.  Without a bias and without
-// dropout the call is the plain forward's.
+// launch on the caller's stream.  Without a bias and without dropout the
+// call is the plain forward's.  Causal dropout without ALiBi runs the
+// two-group layout (eight waves over a 128-row block at two waves per SIMD,
+// as the plain causal forward), where another wave's matrix work covers the
+// generator's; everything else runs workgroups of four waves at one wave per
+// SIMD, whose registers leave room for the bias tile loaded a step ahead.
+// Same-process timing on the [1, 4096, 16, 128] causal workload (us, four
+// waves -> two groups): dropout 0.1 151 -> 126, with a [4096, 4096] bias
+// 194 -> 177; a bias alone 153 -> 159 (so it keeps four waves).
 #include <hip/hip_runtime.h>
 
 #include <cmath>
@@ -20,6 +26,12 @@ namespace {
 
 template <class T, int D, bool C, bool M, bool A>
 void launch_ext(const FwdArgs& args, hipStream_t st) {
+  if constexpr (C && !A) {
+    if (args.drop_thr != 0u) {
+      hipLaunchKernelGGL((fwd_kernel<T, D, C, M, A, 8, false, true, 2>), dim3(args.nitems), dim3(512), 0, st, args);
+      return;
+    }
+  }
   hipLaunchKernelGGL((fwd_kernel<T, D, C, M, A, 4, false, true>), dim3(args.nitems), dim3(256), 0, st, args);
 }
 
