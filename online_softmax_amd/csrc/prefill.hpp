@@ -317,7 +317,14 @@ __global__ __launch_bounds__(NW * 64, EXT && NG == 1 ? 1 : 2) void fwd_kernel(Fw
   // Sweeps that start on their last tiles: the dense band order above, and
   // in block-sparse mode the whole selected list from its last tile down.
   constexpr bool DESC = CAUSAL && ALIBI;
-  if constexpr (MASK && DESC) {
+  // The padding scan decides the sweep's first tiles here (the band below
+  // the last kept key).  In block-sparse mode it runs first; in the dense
+  // kernel the first tiles are copied as if nothing were cleared, together
+  // with Q and the scan's own loads, and copied again in the rare case that
+  // the scan moves them (the band below a cleared tail).
+  constexpr bool SCAN_FIRST = MASK && DESC && SPARSE;
+  constexpr bool SCAN_SPEC = MASK && DESC && !SPARSE;
+  if constexpr (SCAN_FIRST) {
     mask_scan();
     nt = min(nt, last_kept >= 0 ? last_kept / BN + 1 : 0);
   }
@@ -375,7 +382,7 @@ __global__ __launch_bounds__(NW * 64, EXT && NG == 1 ? 1 : 2) void fwd_kernel(Fw
   // positions, so with the band first the rows of group 0 whose diagonal is
   // the band's second tile would start on key 0.  Otherwise the order is
   // plain 0 .. nt-1.
-  const int nb = BAND ? min(nt, BM / BN) : 0;
+  int nb = BAND ? min(nt, BM / BN) : 0;
   auto tile_of = [&](int it) -> int {
     if constexpr (SPARSE) return __builtin_amdgcn_readfirstlane((int)Tl[DESC ? nt - 1 - it : it]);
     else if constexpr (NG == 2 && BAND) return nt - 1 - it;
@@ -383,7 +390,7 @@ __global__ __launch_bounds__(NW * 64, EXT && NG == 1 ? 1 : 2) void fwd_kernel(Fw
   };
   // Iteration t stages the tiles of sweep positions NG t .. NG t + NG - 1
   // (those below nt), the one of group j at offset j BN D of the buffer.
-  const int nti = (nt + NG - 1) / NG;  // iterations of the sweep
+  int nti = (nt + NG - 1) / NG;  // iterations of the sweep
   auto issue_k = [&](int t) {
 #pragma unroll
     for (int j = 0; j < NG; ++j) {
@@ -408,12 +415,15 @@ __global__ __launch_bounds__(NW * 64, EXT && NG == 1 ? 1 : 2) void fwd_kernel(Fw
   auto wtile = [&](int t) -> int { return tile_of(NG * t + gw); };
 
   // Prologue copies: K of iterations 0..NS-1, V of iterations 0..NS-2.
+  auto prologue_copies = [&]() {
 #pragma unroll
-  for (int j = 0; j < NS; ++j)
-    if (j < nti) issue_k(j);
+    for (int j = 0; j < NS; ++j)
+      if (j < nti) issue_k(j);
 #pragma unroll
-  for (int j = 0; j < NS - 1; ++j)
-    if (j < nti) issue_v(j);
+    for (int j = 0; j < NS - 1; ++j)
+      if (j < nti) issue_v(j);
+  };
+  prologue_copies();
 
   // Q^T as the B operand: lane (row li, half g) holds q[row][16kk + 8g .. +7].
   // A negative scale is applied as |scale| on negated Q (exact in fp16/bf16),
@@ -425,13 +435,27 @@ __global__ __launch_bounds__(NW * 64, EXT && NG == 1 ? 1 : 2) void fwd_kernel(Fw
   {
     const uint16_t* qp = a.q + ((size_t)(b * (size_t)a.S_q + (qvalid ? qi : 0)) * a.H_q + h) * D + 8 * g;
 #pragma unroll
-    for (int kk = 0; kk < KK; ++kk) {
-      qreg[kk] = qvalid ? *(const u32x4*)(qp + 16 * kk) : (u32x4){0, 0, 0, 0};
-      qreg[kk] ^= qflip;
-      // Keep the flipped values as the loop-invariant operands (otherwise the
-      // compiler re-applies the flip inside the key loop).
-      __asm__ volatile("" : "+v"(qreg[kk]));
+    for (int kk = 0; kk < KK; ++kk) qreg[kk] = qvalid ? *(const u32x4*)(qp + 16 * kk) : (u32x4){0, 0, 0, 0};
+  }
+  if constexpr (SCAN_SPEC) {
+    mask_scan();
+    const int ntk = min(nt, last_kept >= 0 ? last_kept / BN + 1 : 0);
+    if (ntk != nt) {
+      // Every copy issued so far has landed (the scan waited for its own
+      // loads, which were issued after them); copy the right tiles.
+      wait_vmem();
+      nt = ntk;
+      nb = BAND ? min(nt, BM / BN) : 0;
+      nti = (nt + NG - 1) / NG;
+      prologue_copies();
     }
+  }
+#pragma unroll
+  for (int kk = 0; kk < KK; ++kk) {
+    qreg[kk] ^= qflip;
+    // Keep the flipped values as the loop-invariant operands (otherwise the
+    // compiler re-applies the flip inside the key loop).
+    __asm__ volatile("" : "+v"(qreg[kk]));
   }
 
   if constexpr (MASK && !DESC) mask_scan();
