@@ -369,6 +369,11 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdArgs a) {
   const int qt0 = CAUSAL ? min(nqt, max(0, (k0 - off) / BQ)) : 0;
   const int per_head = nqt - qt0;
   const int niter = per_head * a.G;
+  // Iteration it takes query head gi = it / per_head and, within it, the
+  // query tiles from the last one down to qt0: every workgroup of a KV head
+  // starts on the same (last) tiles, so their reads of Q and dO meet in L2
+  // (from the diagonal up, each would start on a tile of its own).
+  auto qtile = [&](const int it, const int gi) { return nqt - 1 - (it - gi * per_head); };
 
   const size_t qrs = (size_t)a.H_q * D;  // q / dout row stride
   // Tile copies: wave 0 copies Q, wave 1 copies dO, wave 2 the rows' {lse2, Di}.
@@ -382,7 +387,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdArgs a) {
     return (uint32_t)(r * qrs * 2 + 16 * (p ^ bwd_swizzle<D>(r)));
   };
   auto issue = [&](int it) {
-    const int gi = it / per_head, qt = qt0 + (it - gi * per_head);
+    const int gi = it / per_head, qt = qtile(it, gi);
     const int h = hk * a.G + gi;
     const int i0 = qt * BQ, rows = min(BQ, a.S_q - i0);
     const int buf = it % NS;
@@ -455,7 +460,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdArgs a) {
       wait_vmem();
     }
     __syncthreads();
-    const int gi = it / per_head, qt = qt0 + (it - gi * per_head);
+    const int gi = it / per_head, qt = qtile(it, gi);
     const int h = hk * a.G + gi;
     const int i0 = qt * BQ;
     // Rows of this tile that see none of the wave's keys contribute nothing;
