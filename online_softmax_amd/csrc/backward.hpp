@@ -21,9 +21,10 @@
 //  * bwd_dkdv_kernel: a workgroup of 4 waves owns 128 keys of one (batch,
 //    KV head), each wave 32 keys whose K and V rows stay in registers; tiles
 //    of 32 query rows of every query head sharing that KV head stream
-//    through LDS (Q, dO, and the rows' lse and Di), S = Q K^T puts one key
-//    per lane, and dV^T += dO^T P and dK^T += Q^T dS accumulate over all
-//    of them, so the grouped heads' contributions sum in registers.
+//    through LDS (Q, dO, and the rows' lse and Di; from the last tile down
+//    to the block's diagonal), S = Q K^T puts one key per lane, and
+//    dV^T += dO^T P and dK^T += Q^T dS accumulate over all of them, so the
+//    grouped heads' contributions sum in registers.
 #pragma once
 #include "common.hpp"
 

@@ -12,8 +12,9 @@
 //  * key/value tiles of 64 rows are copied from global memory straight into
 //    LDS (buffer loads with the LDS destination, 16 bytes per lane) through a
 //    ring of NS buffers per tensor; the buffer bounds return zeros past the
-//    last key.  Copies are issued NS-2 iterations ahead of the barrier that
-//    publishes them and awaited with a partial vmcnt;
+//    last key.  Iteration t issues K of tile t+NS and V of tile t+NS-1; they
+//    are awaited before the barrier that closes iteration t+NS-2 (with the
+//    two buffers used here, iteration t's own);
 //  * LDS rows are unpadded; 16-byte chunks are placed at (chunk XOR f(row))
 //    so that the K reads (16 rows, one chunk) and the transposed V reads
 //    (4 consecutive rows, 4 chunks) each touch distinct banks;
@@ -53,6 +54,15 @@
 //    maximum; dropout keeps or zeroes each probability by a 16-bit half of a
 //    Philox4x32-10 word of its (row, key) position, after the row sum has
 //    taken it;
+//  * two-group mode (NG = 2, the causal forward when 128-row blocks are
+//    needed to balance the CUs, and causal dropout): eight waves over one
+//    128-row block in two groups of four that own the same rows and take
+//    alternate tiles (each iteration stages one tile per group); at the end
+//    group 1 hands its state to group 0 through LDS;
+//  * persistent schedule (PERSIST, large eight-wave grids): one workgroup per
+//    CU works through a list of (batch, head) units, each a complementary
+//    pair of causal blocks (x and nmb - 1 - x) or one block, so that every
+//    unit carries the same work and a CU never waits for a new workgroup;
 //  * the reference maximum is raised only when a tile's maximum exceeds it by
 //    more than kRescaleSlack (base 2): the final out = numerator / denominator
 //    and lse = reference + log(denominator) are exact for any reference, and
