@@ -62,31 +62,54 @@ __device__ inline int bwd_swizzle(int r) {
   else return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);
 }
 
-// Di = <dout_i, out_i> and the base-2 lse of every (batch, head, row).
+// Di = <dout_i, out_i> and the base-2 lse of every (batch, head, row).  A
+// row's D values are read by D / 8 consecutive lanes, 16 bytes each, so that
+// one wave instruction reads 64 / (D / 8) whole rows; each wave takes kPreRounds
+// such row groups, all loads in flight before any product.
+constexpr int kPreRounds = 4;
+template <int D>
+constexpr int pre_rows_per_block() { return 4 * kPreRounds * (64 / (D / 8)); }
+
 template <class T, int D>
 __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdArgs a) {
+  constexpr int LPR = D / 8, RPW = 64 / LPR;  // lanes per row, rows per wave instruction
   const int64_t n = (int64_t)a.B * a.H_q * a.S_q;
-  const int64_t x = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (x >= n) return;
-  const int i = (int)(x % a.S_q);
-  const int64_t bh = x / a.S_q;
-  const int h = (int)(bh % a.H_q), b = (int)(bh / a.H_q);
-  const size_t row = (((size_t)b * a.S_q + i) * a.H_q + h) * D;
-  const u32x4* po = (const u32x4*)(a.out + row);
-  const u32x4* pd = (const u32x4*)(a.dout + row);
-  float acc = 0.f;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int sub = lane % LPR, rl = lane / LPR;
+  const int64_t x0 = ((int64_t)blockIdx.x * 4 + w) * (kPreRounds * RPW) + rl;
+  u32x4 o4[kPreRounds], d4[kPreRounds];
 #pragma unroll
-  for (int c = 0; c < D / 8; ++c) {
-    const u32x4 o4 = po[c], d4 = pd[c];
+  for (int r = 0; r < kPreRounds; ++r) {
+    const int64_t x = x0 + r * RPW;
+    if (x < n) {
+      const int i = (int)(x % a.S_q);
+      const int64_t bh = x / a.S_q;
+      const int h = (int)(bh % a.H_q), b = (int)(bh / a.H_q);
+      const size_t row = (((size_t)b * a.S_q + i) * a.H_q + h) * D + 8 * sub;
+      o4[r] = *(const u32x4*)(a.out + row);
+      d4[r] = *(const u32x4*)(a.dout + row);
+    } else {
+      o4[r] = (u32x4){0, 0, 0, 0};
+      d4[r] = (u32x4){0, 0, 0, 0};
+    }
+  }
+#pragma unroll
+  for (int r = 0; r < kPreRounds; ++r) {
+    float acc = 0.f;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      const f32x2 of = T::unpack2(o4[e]), df = T::unpack2(d4[e]);
+      const f32x2 of = T::unpack2(o4[r][e]), df = T::unpack2(d4[r][e]);
       acc = fmaf(of[0], df[0], acc);
       acc = fmaf(of[1], df[1], acc);
     }
+#pragma unroll
+    for (int k = LPR / 2; k >= 1; k >>= 1) acc += __shfl_xor(acc, k);
+    const int64_t x = x0 + r * RPW;
+    if (x < n && sub == 0) {
+      const float l = a.lse[x];
+      a.ld[x] = make_float2(l == kNegInf ? __builtin_huge_valf() : l * kLog2e, acc);
+    }
   }
-  const float l = a.lse[x];
-  a.ld[x] = make_float2(l == kNegInf ? __builtin_huge_valf() : l * kLog2e, acc);
 }
 
 // ---------------------------------------------------------------------------

@@ -30,7 +30,8 @@ void launch_bwd_main(const BwdArgs& args, hipStream_t st) {
 template <class T, int D>
 void dispatch_bwd(const BwdArgs& args, bool causal, bool mask, bool alibi, hipStream_t st) {
   const int64_t rows = (int64_t)args.B * args.H_q * args.S_q;
-  if (rows > 0) hipLaunchKernelGGL((bwd_pre_kernel<T, D>), dim3((unsigned)((rows + 255) / 256)), dim3(256), 0, st, args);
+  constexpr int rpb = pre_rows_per_block<D>();
+  if (rows > 0) hipLaunchKernelGGL((bwd_pre_kernel<T, D>), dim3((unsigned)((rows + rpb - 1) / rpb)), dim3(256), 0, st, args);
   const int key = (causal ? 4 : 0) | (mask ? 2 : 0) | (alibi ? 1 : 0);
   switch (key) {
     case 0: launch_bwd_main<T, D, false, false, false>(args, st); break;
