@@ -12,7 +12,7 @@ which alone exceeds 5e-3 for bf16 values of magnitude 2 or more and takes
 most of it in [1, 2).  The last term is the rounding of each probability to
 the input type before the P.V product (as the pages' kernels do, and as the
 matrix cores require): it moves an output by at most u * sum_j w_j |v_j| (w
-the row's softmax weights, u = 2^-9 for bfloat16, 2^-12 for float16).  Over
+the row's softmax weights, u = 2^-8 for bfloat16, 2^-11 for float16).  Over
 many keys these errors average out; over the few keys that carry a row's
 weight under a steep ALiBi slope or a sparse mask they do not.  Every check
 prints its maximum error, the count of elements above the literal 5e-3 and
@@ -24,6 +24,7 @@ import numpy as np
 import torch
 
 import oracle
+from oracle.attention import _scores, _softmax_rows
 from workloads import to_f64
 
 OUT_ATOL = 5e-3
@@ -70,11 +71,40 @@ def assert_out_close(gpu, ref, dtype, what="", extra=None):
 
 def p_rounding(abs_v_out, dtype):
     """u * sum_j w_j |v_j|: the bound on what rounding the probabilities to
-    the input type before P.V moves an output (u = 2^-9 for bfloat16, 2^-12
+    the input type before P.V moves an output (u = 2^-8 for bfloat16, 2^-11
     for float16).  ``abs_v_out`` is the oracle's output with |v| in place of
     v, i.e. sum_j w_j |v_j| per element."""
-    u = 2.0 ** -9 if dtype == torch.bfloat16 else 2.0 ** -12
+    u = 2.0 ** -8 if dtype == torch.bfloat16 else 2.0 ** -11
     return u * np.asarray(abs_v_out, np.float64)
+
+
+def grad_rounding(inp, dout, dtype):
+    """Per-element bound on what rounding the second products' operands to
+    the input type moves the gradients: ``(u * scale * |dS| |k|,
+    u * scale * |dS|^T |q|, u * P^T |dout|)`` for ``(dq, dk, dv)``, summed over
+    the query heads of a key/value head like the gradients themselves.
+
+    dS and P are the exact float64 ones of the backward's definition (the
+    oracle's visibility, bias, score and softmax steps); rounding each dS or
+    P element by at most u relative moves a product by at most u times the
+    sum of the absolute terms.  u = 2^-8 for bfloat16, 2^-11 for float16."""
+    w = inp.w
+    q, k, v, do = to_f64(inp.q), to_f64(inp.k), to_f64(inp.v), np.asarray(dout, np.float64)
+    G = w.H_q // w.H_kv
+    u = 2.0 ** -8 if dtype == torch.bfloat16 else 2.0 ** -11
+    eq, ek, ev = np.zeros_like(q), np.zeros_like(k), np.zeros_like(v)
+    for b in range(w.B):
+        keep = oracle.visible(w.S_q, w.S_k, w.causal, None if inp.mask is None else inp.mask.numpy()[b])
+        for h in range(w.H_q):
+            hk = h // G
+            bias = None if inp.slopes is None else oracle.alibi_bias(float(inp.slopes[h]), w.S_q, w.S_k)
+            P, _ = _softmax_rows(_scores(q[b, :, h], k[b, :, hk], w.scale, keep, bias))
+            dP = do[b, :, h] @ v[b, :, hk].T
+            adS = np.abs(P * (dP - (P * dP).sum(axis=1, keepdims=True)))
+            eq[b, :, h] = w.scale * (adS @ np.abs(k[b, :, hk]))
+            ek[b, :, hk] += w.scale * (adS.T @ np.abs(q[b, :, h]))
+            ev[b, :, hk] += P.T @ np.abs(do[b, :, h])
+    return u * eq, u * ek, u * ev
 
 
 def assert_lse_close(gpu, ref, what=""):

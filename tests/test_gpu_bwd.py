@@ -13,6 +13,16 @@ the operands of the second products (dS and P) and the forward's output to
 the input format, so it scales with the format's unit roundoff: bfloat16
 keeps 8 significant bits against float16's 11, and its ``atol`` is
 3e-3 * 2**3 = 2.4e-2.
+
+The page's figure is a measured maximum at its shapes, not a bound that holds
+at every size: a gradient of a key/value head sums the terms of all its query
+heads and rows, and a dS or P term rounded to the input format moves it by up
+to u times that term.  As for the forward output's probability term, the
+bound adds ``u * sum |term|`` per element (``parity.grad_rounding``); the
+forward output's own error, which enters through Di, stays within ``atol``.
+At 8 query heads per key/value head (128 on 16) in bfloat16, the rounding
+of dS, P and the output alone (emulated on the CPU in float64) takes dk and
+dv past the plain ``atol + ulp/2`` by up to 1.5x.
 """
 import numpy as np
 import pytest
@@ -20,7 +30,7 @@ import torch
 
 import online_softmax_amd as sa
 import oracle
-from parity import half_ulp, to_dev
+from parity import grad_rounding, half_ulp, to_dev
 from workloads import WORKLOADS, Workload, make_dout, make_inputs, to_f64
 
 pytestmark = pytest.mark.gpu
@@ -49,15 +59,16 @@ def check(inp, what=""):
                                key_padding_mask=None if inp.mask is None else inp.mask.numpy(),
                                alibi_slopes=None if inp.slopes is None else inp.slopes.numpy())
     dt = torch.float16 if w.dtype == "fp16" else torch.bfloat16
-    for name, g, r in zip(("dq", "dk", "dv"), got, ref):
+    extra = grad_rounding(inp, to_f64(dout), dt)
+    for name, g, r, x in zip(("dq", "dk", "dv"), got, ref, extra):
         g = to_f64(g.cpu())
         assert np.isfinite(g).all(), f"{what or w.name}: non-finite {name}"
         err = np.abs(g - r)
-        bound = GRAD_ATOL[w.dtype] + half_ulp(r, dt)
-        fp16_bound = GRAD_ATOL["fp16"] + half_ulp(r, dt)
+        plain = GRAD_ATOL[w.dtype] + half_ulp(r, dt)
+        bound = plain + x
         print(f"    {name}: max abs err {err.max(initial=0):.3e}  max |ref| {np.abs(r).max(initial=0):.3e}  "
               f"worst err/bound {np.max(err / bound, initial=0):.3f} "
-              f"(against the float16 bound: {np.max(err / fp16_bound, initial=0):.3f})", flush=True)
+              f"({np.max(err / plain, initial=0):.3f} without the rounding term)", flush=True)
         assert (err <= bound).all(), f"{what or w.name}: {int((err > bound).sum())} {name} elements beyond bound"
     return got
 
@@ -84,6 +95,19 @@ def test_bwd_cases(w):
 
 def test_bwd_config2_full():
     check(make_inputs(WORKLOADS["c2_causal_pad16"]))
+
+
+@pytest.mark.parametrize("w", [
+    # 8 query heads per key/value head: dk and dv sum 8 heads x 300 rows; ragged ends, padding, ALiBi
+    Workload("b_gqa8_causal_all", 4, 300, 300, 128, 16, 64, "bf16", causal=True, alibi=True, random_tail=60,
+             seed=75),
+    # 8 query heads per key/value head, queries shorter than keys
+    Workload("b_gqa8_plain", 2, 300, 340, 64, 8, 64, "fp16", seed=76),
+], ids=lambda w: w.name)
+def test_bwd_large_gqa(w):
+    """Grids of many workgroups, with large query-head groups per key/value
+    head; checked in full."""
+    check(make_inputs(w))
 
 
 def test_bwd_empty_rows_and_keys():

@@ -238,3 +238,44 @@ def test_bwd_mutants_run_and_differ(name):
 def test_bwd_pins_reject_planted_mistakes(name):
     failed = [p.__name__ for p in PINS if not _safe(p, MUTANTS[name])]
     assert failed, f"no pin catches the planted mistake: {name}"
+
+
+def _bf16(x):
+    return torch.from_numpy(np.ascontiguousarray(x)).to(torch.bfloat16).double().numpy()
+
+
+def test_grad_rounding_term_bounds_operand_rounding():
+    """The GPU tests' gradient rounding term (``parity.grad_rounding``): its
+    dv part is u times the oracle's dv of |dout|, and a float64 backward whose
+    dS and P are rounded to bfloat16 before the second products stays within
+    it element by element."""
+    from parity import grad_rounding
+    from workloads import Workload, make_dout, make_inputs, to_f64
+    w = Workload("grad_term", 2, 40, 56, 8, 2, 16, "bf16", causal=True, alibi=True, random_tail=12, seed=79)
+    inp = make_inputs(w)
+    do = to_f64(make_dout(w))
+    q, k, v = to_f64(inp.q), to_f64(inp.k), to_f64(inp.v)
+    mask, sl = inp.mask.numpy(), inp.slopes.numpy()
+    eq, ek, ev = grad_rounding(inp, do, torch.bfloat16)
+    u = 2.0 ** -8
+    dv_abs = oracle.attention_bwd(q, k, v, np.abs(do), w.scale, causal=True, key_padding_mask=mask,
+                                  alibi_slopes=sl)[2]
+    assert np.allclose(ev, u * dv_abs, rtol=1e-12, atol=0)
+    ref = oracle.attention_bwd(q, k, v, do, w.scale, causal=True, key_padding_mask=mask, alibi_slopes=sl)
+    G = w.H_q // w.H_kv
+    dq, dk, dv = np.zeros_like(q), np.zeros_like(k), np.zeros_like(v)
+    for b in range(w.B):
+        keep = oracle.visible(w.S_q, w.S_k, True, mask[b])
+        for h in range(w.H_q):
+            hk = h // G
+            P, _ = oatt._softmax_rows(oatt._scores(q[b, :, h], k[b, :, hk], w.scale, keep,
+                                                   oracle.alibi_bias(float(sl[h]), w.S_q, w.S_k)))
+            dP = do[b, :, h] @ v[b, :, hk].T
+            dS = _bf16(P * (dP - (P * dP).sum(axis=1, keepdims=True)))
+            dq[b, :, h] = w.scale * (dS @ k[b, :, hk])
+            dk[b, :, hk] += w.scale * (dS.T @ q[b, :, h])
+            dv[b, :, hk] += _bf16(P).T @ do[b, :, h]
+    for g, r, e in zip((dq, dk, dv), ref, (eq, ek, ev)):
+        err = np.abs(g - r)
+        assert (err <= e * (1 + 1e-9) + 1e-12).all()
+        assert err.max() > 0.1 * e.max()      # the term is not vacuous at this size
