@@ -24,6 +24,8 @@ At 8 query heads per key/value head (128 on 16) in bfloat16, the rounding
 of dS, P and the output alone (emulated on the CPU in float64) takes dk and
 dv past the plain ``atol + ulp/2`` by up to 1.5x.
 """
+import dataclasses
+
 import numpy as np
 import pytest
 import torch
@@ -31,7 +33,7 @@ import torch
 import online_softmax_amd as sa
 import oracle
 from parity import grad_rounding, half_ulp, to_dev
-from workloads import WORKLOADS, Workload, make_dout, make_inputs, to_f64
+from workloads import WORKLOADS, Inputs, Workload, make_dout, make_inputs, to_f64
 
 pytestmark = pytest.mark.gpu
 GRAD_ATOL = {"fp16": 3e-3, "bf16": 3e-3 * 2 ** 3}
@@ -54,6 +56,13 @@ def check(inp, what=""):
           flush=True)
     dout = make_dout(w)
     got = run_bwd(inp, dout)
+    compare(inp, dout, got, what)
+    return got
+
+
+def compare(inp, dout, got, what=""):
+    """dq, dk, dv of the GPU (``got``) against the oracle's, element by element."""
+    w = inp.w
     ref = oracle.attention_bwd(to_f64(inp.q), to_f64(inp.k), to_f64(inp.v), to_f64(dout), w.scale,
                                causal=w.causal,
                                key_padding_mask=None if inp.mask is None else inp.mask.numpy(),
@@ -70,7 +79,6 @@ def check(inp, what=""):
               f"worst err/bound {np.max(err / bound, initial=0):.3f} "
               f"({np.max(err / plain, initial=0):.3f} without the rounding term)", flush=True)
         assert (err <= bound).all(), f"{what or w.name}: {int((err > bound).sum())} {name} elements beyond bound"
-    return got
 
 
 CASES = [
@@ -108,6 +116,30 @@ def test_bwd_large_gqa(w):
     """Grids of many workgroups, with large query-head groups per key/value
     head; checked in full."""
     check(make_inputs(w))
+
+
+@pytest.mark.parametrize("name,heads", [("c3_causal_4096", [(0, 0), (0, 11)]),
+                                        ("c5_alibi_8192", [(0, 0), (1, 29)])])
+def test_bwd_full_size_sampled_heads(name, heads):
+    """The backward at the benchmark's full sizes, in the launch configuration
+    it times: the gradients of a few (batch, head) slices checked in full
+    against the oracle run on that slice alone.  These shapes have as many
+    key/value heads as query heads, so a key/value head's dk and dv come from
+    its one query head; the slice carries its batch row's padding and its
+    head's ALiBi slope."""
+    w = WORKLOADS[name]
+    assert w.H_q == w.H_kv
+    inp = make_inputs(w)
+    dout = make_dout(w)
+    print(f"[bwd] {name} full size B={w.B} S={w.S_q} H={w.H_q} D={w.D} {w.dtype}; heads {heads}", flush=True)
+    got = [g.cpu() for g in run_bwd(inp, dout)]
+    for b, h in heads:
+        one = lambda t: t[b:b + 1, :, h:h + 1].contiguous()
+        sub = Inputs(dataclasses.replace(w, B=1, H_q=1, H_kv=1), one(inp.q), one(inp.k), one(inp.v),
+                     None if inp.mask is None else inp.mask[b:b + 1].contiguous(),
+                     None if inp.slopes is None else inp.slopes[h:h + 1].contiguous())
+        print(f"  slice b={b} h={h}", flush=True)
+        compare(sub, one(dout), [one(g) for g in got], f"{name} b={b} h={h}")
 
 
 def test_bwd_empty_rows_and_keys():
