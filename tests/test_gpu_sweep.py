@@ -1,7 +1,8 @@
 """Seeded sweep of every compiled instance against the oracle.
 
-Each entry point is built for {float16, bfloat16} x D {64, 128} x {causal}
-x {key-padding mask} x {ALiBi}.  For every combination one shape is drawn
+Each entry point (forward, backward, block-sparse, extended, decode) is
+built for {float16, bfloat16} x D {64, 128} x {causal} x {key-padding mask}
+x {ALiBi} (decode: no causal rule).  For every combination one shape is drawn
 from a seeded generator (batch, query heads per key/value head, ragged
 query and key lengths, masked tail lengths up to all the keys) and the
 whole output is compared with the oracle, to the same bounds as the other
@@ -17,10 +18,11 @@ import torch
 import online_softmax_amd as sa
 import test_gpu_bwd as bwd
 import test_gpu_decode as dec
+import test_gpu_ext as ext
 import test_gpu_fwd as fwd
 import test_gpu_sparse as sparse
 from parity import assert_lse_close, assert_out_close, oracle_for, p_rounding
-from workloads import Workload, make_block_mask, make_inputs
+from workloads import Workload, make_bias, make_block_mask, make_inputs
 
 pytestmark = pytest.mark.gpu
 
@@ -32,7 +34,7 @@ def _cid(c):
     return f"{dt}_d{D}" + "_causal" * causal + "_mask" * mask + "_alibi" * alibi
 
 
-KIND = {"fwd": 1, "bwd": 2, "sparse": 3}
+KIND = {"fwd": 1, "bwd": 2, "sparse": 3, "ext": 4}
 
 
 def _shape(kind, i, c, max_s, groups, max_b=3, max_hkv=3):
@@ -62,6 +64,20 @@ def test_sweep_backward(i, c):
 def test_sweep_block_sparse(i, c):
     w = _shape("sparse", i, c, 400, (1, 2, 4))
     sparse.check(make_inputs(w), make_block_mask(w, keep=0.3))
+
+
+@pytest.mark.parametrize("i,c", list(enumerate(COMBOS)), ids=[_cid(c) for c in COMBOS])
+def test_sweep_extended(i, c):
+    """The extended forward with a seeded additive mask at one of its four
+    broadcast shapes and/or dropout (at least one of them, else the call is
+    the plain forward's)."""
+    w = _shape("ext", i, c, 300, (1, 2, 3))
+    r = np.random.default_rng([KIND["ext"], 100 + i])
+    kind = [None, "bhqk", "b1qk", "qk", "b11k"][int(r.integers(0, 5))]
+    p = [0.0, 0.15, 0.4][int(r.integers(0, 3))]
+    if kind is None and p == 0.0:
+        p = 0.15
+    ext.check(make_inputs(w), None if kind is None else make_bias(w, kind), p, seed=0x5EED0000 + i, offset=i)
 
 
 DEC_COMBOS = [c for c in COMBOS if not c[2]]  # one query row: the causal rule hides nothing
