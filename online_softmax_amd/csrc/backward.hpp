@@ -404,7 +404,9 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdArgs a) {
   // Copy u of a lane fills LDS row r, position p, from global chunk
   // p ^ f(r); the offsets are recomputed at each tile (from a lane index the
   // compiler cannot see through) rather than held in registers for the whole
-  // sweep.
+  // sweep.  The swizzle f repeats every 16 rows, which is every P = D / 32
+  // copies: copy u is copy u mod P of the lane, u / P times 16 rows further
+  // on, so only P offsets are formed and the rest add a scalar.
   auto toff = [&](const int ln, const int u) -> uint32_t {
     const int byte = u * 1024 + 16 * ln;
     const int r = byte / (2 * D), p = (byte % (2 * D)) / 16;
@@ -421,8 +423,14 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdArgs a) {
       uint16_t* dst = w == 0 ? Qs[buf] : Os[buf];
       int ln = lane;
       __asm__ volatile("" : "+v"(ln));
+      constexpr int P = D / 32;
+      static_assert(NI % P == 0 && 1024 * P == 16 * 2 * D, "P copies span 16 rows");
+      uint32_t o0[P];
 #pragma unroll
-      for (int u = 0; u < NI; ++u) load_lds16(r, dst + u * 512, toff(ln, u));
+      for (int c = 0; c < P; ++c) o0[c] = toff(ln, c);
+#pragma unroll
+      for (int u = 0; u < NI; ++u)
+        load_lds16(r, dst + u * 512, o0[u % P] + (uint32_t)(u / P) * (uint32_t)(32 * qrs));
     } else if (w == 2) {
       // BQ float2 = 256 bytes: 16 lanes of 16 bytes (the others would write
       // past Ls[buf]); rows past S_q read zero.
