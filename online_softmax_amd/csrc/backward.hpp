@@ -357,8 +357,9 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdArgs a) {
   constexpr int NW = 4, BK = 32 * NW, BQ = 32, NS = 2;
   constexpr int KK = D / 16, DB = D / 32;
   constexpr int NI = BQ * D * 2 / 1024;  // 1 KiB copies per tensor per tile (all by one wave each)
-  __shared__ __attribute__((aligned(1024))) uint16_t Qs[NS][BQ * D];
-  __shared__ __attribute__((aligned(1024))) uint16_t Os[NS][BQ * D];
+  // Q and dO tiles of one buffer side by side, so that a dO fragment is read
+  // at its Q fragment's address plus a constant (the reads' offset field).
+  __shared__ __attribute__((aligned(1024))) uint16_t QOs[NS][2][BQ * D];
   __shared__ __attribute__((aligned(256))) float2 Ls[NS][BQ];
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -420,7 +421,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdArgs a) {
     if (w == 0 || w == 1) {
       const uint16_t* base = (w == 0 ? a.q : a.dout) + (((size_t)b * a.S_q + i0) * a.H_q + h) * D;
       const auto r = buffer_rsrc(base, (uint32_t)((rows - 1) * qrs * 2 + 2 * D));
-      uint16_t* dst = w == 0 ? Qs[buf] : Os[buf];
+      uint16_t* dst = QOs[buf][w];
       int ln = lane;
       __asm__ volatile("" : "+v"(ln));
       constexpr int P = D / 32;
@@ -499,8 +500,8 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdArgs a) {
     // a tile whose rows all end before the wave's first key is skipped.
     const bool active = !CAUSAL || i0 + BQ - 1 + off >= kw0;
     if (active) {
-      const uint16_t* qt_ = Qs[it % NS];
-      const uint16_t* ot_ = Os[it % NS];
+      const uint16_t* qt_ = QOs[it % NS][0];
+      const uint16_t* ot_ = qt_ + BQ * D;
       const float2* lt = Ls[it % NS];
       if (ALIBI && gi != slope_head) {
         slope_head = gi;
