@@ -28,7 +28,10 @@
 //    is swept first (last tile down), then the tiles from key 0 up: every
 //    wave starts on its own diagonal tile, where the largest biases sit (the
 //    running maximum then settles at once), while the workgroups of a head
-//    still share the tiles from key 0 in L2; otherwise tiles go in key order;
+//    still share the tiles from key 0 in L2 (under the persistent schedule the
+//    second block of a unit sweeps from its last tile down, so that the CUs
+//    of one head read the same tiles at the same time); otherwise tiles go in
+//    key order;
 //  * software pipeline: iteration t runs S^T of the next tile on the matrix
 //    cores while the vector units form the probabilities of tile t, then
 //    P·V of tile t, then prepares the next tile;
@@ -239,6 +242,7 @@ __global__ __launch_bounds__(NW * 64, EXT && NG == 1 ? 1 : 2) void fwd_kernel(Fw
   const int gw = NG == 1 ? 0 : w / NWG;  // this wave's group
   const int wi = w - gw * NWG;           // and its place in the group
   int bh, mb;
+  bool second = false;  // persistent schedule: the unit's second (lighter) block
   if constexpr (!PERSIST) {
     const int item = xcd_contiguous(blockIdx.x, a.nitems);
     bh = item / a.nmb;
@@ -253,6 +257,7 @@ __global__ __launch_bounds__(NW * 64, EXT && NG == 1 ? 1 : 2) void fwd_kernel(Fw
     bh = q / upb;
     const int x = q - bh * upb;
     mb = CAUSAL && half == 0 ? a.nmb - 1 - x : x;
+    second = CAUSAL && half != 0;
   }
   const int b = bh / a.H_q, h = bh - b * a.H_q, hk = h / a.G;
   const int m0 = mb * BM;
@@ -392,7 +397,15 @@ __global__ __launch_bounds__(NW * 64, EXT && NG == 1 ? 1 : 2) void fwd_kernel(Fw
   // positions, so with the band first the rows of group 0 whose diagonal is
   // the band's second tile would start on key 0.  Otherwise the order is
   // plain 0 .. nt-1.
-  int nb = BAND ? min(nt, BM / BN) : 0;
+  // Under the persistent schedule the second block of a unit sweeps all its
+  // tiles from the last one down.  The CUs working on the units of one head
+  // reach their second blocks at different times (after first blocks of
+  // different lengths); in descending order they still stand on the same
+  // tile at each moment -- block x starts its descent at key block x after
+  // the nmb - x key blocks of its first block, so at sweep time t every such
+  // CU is at key block nmb - t -- and their reads are shared in L2.
+  auto band_tiles = [&]() { return BAND ? (second ? nt : min(nt, BM / BN)) : 0; };
+  int nb = band_tiles();
   auto tile_of = [&](int it) -> int {
     if constexpr (SPARSE) return __builtin_amdgcn_readfirstlane((int)Tl[DESC ? nt - 1 - it : it]);
     else if constexpr (NG == 2 && BAND) return nt - 1 - it;
@@ -455,7 +468,7 @@ __global__ __launch_bounds__(NW * 64, EXT && NG == 1 ? 1 : 2) void fwd_kernel(Fw
       // loads, which were issued after them); copy the right tiles.
       wait_vmem();
       nt = ntk;
-      nb = BAND ? min(nt, BM / BN) : 0;
+      nb = band_tiles();
       nti = (nt + NG - 1) / NG;
       prologue_copies();
     }

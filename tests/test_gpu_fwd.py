@@ -325,6 +325,11 @@ PERSISTENT = [
     Workload("persist_groups_odd_f16_d64", 4, 640, 640, 64, 16, 64, "fp16", causal=True, random_tail=100,
              seed=161),
     Workload("persist_groups_alibi_bf16_d64", 4, 600, 640, 64, 8, 64, "bf16", causal=True, alibi=True, seed=162),
+    # 256-row blocks under the causal rule with ALiBi and padding (the c5
+    # layout): units of blocks 3 and 0, 2 and 1; the second block of each
+    # unit sweeps from its last tile down
+    Workload("persist_w8_alibi_mask_bf16_d64", 4, 1024, 1024, 64, 64, 64, "bf16", causal=True, alibi=True,
+             random_tail=300, seed=164),
 ]
 
 
