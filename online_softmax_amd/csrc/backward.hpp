@@ -286,7 +286,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
           dp[jb] = T::mma(*(const u32x4*)&vt[off16], doreg[kk], dp[jb]);
         }
       const bool padded = MASK && n0 + BN > pad_start;
-      const bool masked = n0 + BN > a.S_k || (CAUSAL && n0 + BN - 1 > wrow0 + off) || MASK;
+      const bool masked = n0 + BN > a.S_k || (CAUSAL && n0 + BN - 1 > wrow0 + off) || padded;
       // Padding bits of the tile's 64 keys (the same for every row): lane l
       // reads the byte of key n0 + l, one ballot gathers them (bit l kept),
       // shifted to this lane's half (keys from 4 g on).
@@ -296,6 +296,20 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
         const bool kept = kl < a.S_k && mrow[kl < a.S_k ? kl : 0] != 0;
         keep = __builtin_amdgcn_ballot_w64(kept) >> (4 * g);
       }
+      // Tiles that no rule hides any key of skip the masking pass.
+      if (masked) {
+#pragma unroll
+        for (int jb = 0; jb < 2; ++jb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int ko = 32 * jb + 8 * (r >> 2) + (r & 3);  // from n0 + 4 g
+            const int kj = n0 + 4 * g + ko;
+            bool vis = kj < a.S_k;
+            if (CAUSAL) vis = vis & (kj <= ipos);
+            if (MASK) vis = vis & (((keep >> ko) & 1u) != 0);
+            s[jb][r] = vis ? s[jb][r] : kNegInf;
+          }
+      }
       uint32_t pk[2][8];
 #pragma unroll
       for (int jb = 0; jb < 2; ++jb)
@@ -304,16 +318,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
           float ds[2];
 #pragma unroll
           for (int e = 0; e < 2; ++e) {
-            float sv = s[jb][r + e];
-            if (masked) {
-              const int ko = 32 * jb + 8 * ((r + e) >> 2) + ((r + e) & 3);  // from n0 + 4 g
-              const int kj = n0 + 4 * g + ko;
-              bool vis = kj < a.S_k;
-              if (CAUSAL) vis = vis && kj <= ipos;
-              if (MASK) vis = vis && ((keep >> ko) & 1u);
-              sv = vis ? sv : kNegInf;
-            }
-            const float p = fast_exp2(fmaf(sv, sc2, -l2));
+            const float p = fast_exp2(fmaf(s[jb][r + e], sc2, -l2));
             ds[e] = p * (dp[jb][r + e] - di);
           }
           pk[jb][r >> 1] = T::pack2(ds[0], ds[1]);
