@@ -622,7 +622,7 @@ def main():
         result["roofline"] = {"bound": "mfma", "achieved": round(ach, 2), "peak": MFMA_PEAK_TFLOPS,
                               "unit": "TFLOP/s", "frac": round(ach / MFMA_PEAK_TFLOPS, 4),
                               "traffic": read_traffic("bwd_kernels", p.w.name),
-                              "kernel": "bwd_pre_kernel + bwd_dq_kernel + bwd_dkdv_kernel (one call)",
+                              "kernel": "bwd_dq_kernel + bwd_dkdv_kernel (one call)",
                               "workload": p.w.name + " backward", "avg_call_ms": round(t, 4),
                               "flops_per_call": p.flops}
     if prefill:

@@ -9,15 +9,16 @@
 //   Di = <dout_i, out_i>,  dP = dout V^T,  dS = P (dP - Di),
 //   dv = P^T dout,  dq = scale dS K,  dk = scale dS^T q.
 //
-// Three kernels, so that every gradient is summed in registers in a fixed
+// Two kernels, so that every gradient is summed in registers in a fixed
 // order (no atomics, bit-reproducible):
-//  * bwd_pre_kernel: per query row, Di and lse in base 2 (+inf for a row
-//    with no visible key, so that its probabilities are 0), as one float2;
 //  * bwd_dq_kernel: the forward's layout (a workgroup of 4 waves owns 128
 //    query rows of one (batch, head); K/V tiles of 64 keys stream through LDS
 //    with direct buffer-to-LDS copies; S^T = K Q^T puts one query per lane):
 //    P^T from the saved lse, dP^T = V dO^T with dO held in registers like Q,
-//    dQ^T += K^T dS^T with K read transposed from LDS;
+//    dQ^T += K^T dS^T with K read transposed from LDS.  It first forms, for
+//    its rows, Di = <dout_i, out_i> and the lse in base 2 (+inf for a row
+//    with no visible key, so that its probabilities are 0), and stores them
+//    as one float2 per row for the next kernel;
 //  * bwd_dkdv_kernel: a workgroup of 4 waves owns 128 keys of one (batch,
 //    KV head), each wave 32 keys whose K and V rows stay in registers; tiles
 //    of 32 query rows of every query head sharing that KV head stream
@@ -42,7 +43,8 @@ struct BwdArgs {
   uint16_t* dv;
   const uint8_t* mask;
   const float* slopes;
-  float2* ld;           // workspace [B, H_q, S_q]: {lse * log2(e) or +inf, Di}
+  float2* ld;           // workspace [B, H_q, S_q]: {lse * log2(e) or +inf, Di},
+                        // written by the dq kernel, read by the dk/dv kernel
   int B, S_q, S_k, H_q, H_kv, G;
   float scale;          // signed
   float scale2;         // |scale| * log2(e)
@@ -60,56 +62,6 @@ template <int D>
 __device__ inline int bwd_swizzle(int r) {
   if constexpr (D == 128) return ((r & 3) << 2) | ((r >> 2) & 3);
   else return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);
-}
-
-// Di = <dout_i, out_i> and the base-2 lse of every (batch, head, row).  A
-// row's D values are read by D / 8 consecutive lanes, 16 bytes each, so that
-// one wave instruction reads 64 / (D / 8) whole rows; each wave takes kPreRounds
-// such row groups, all loads in flight before any product.
-constexpr int kPreRounds = 4;
-template <int D>
-constexpr int pre_rows_per_block() { return 4 * kPreRounds * (64 / (D / 8)); }
-
-template <class T, int D>
-__global__ __launch_bounds__(256) void bwd_pre_kernel(BwdArgs a) {
-  constexpr int LPR = D / 8, RPW = 64 / LPR;  // lanes per row, rows per wave instruction
-  const int64_t n = (int64_t)a.B * a.H_q * a.S_q;
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  const int sub = lane % LPR, rl = lane / LPR;
-  const int64_t x0 = ((int64_t)blockIdx.x * 4 + w) * (kPreRounds * RPW) + rl;
-  u32x4 o4[kPreRounds], d4[kPreRounds];
-#pragma unroll
-  for (int r = 0; r < kPreRounds; ++r) {
-    const int64_t x = x0 + r * RPW;
-    if (x < n) {
-      const int i = (int)(x % a.S_q);
-      const int64_t bh = x / a.S_q;
-      const int h = (int)(bh % a.H_q), b = (int)(bh / a.H_q);
-      const size_t row = (((size_t)b * a.S_q + i) * a.H_q + h) * D + 8 * sub;
-      o4[r] = *(const u32x4*)(a.out + row);
-      d4[r] = *(const u32x4*)(a.dout + row);
-    } else {
-      o4[r] = (u32x4){0, 0, 0, 0};
-      d4[r] = (u32x4){0, 0, 0, 0};
-    }
-  }
-#pragma unroll
-  for (int r = 0; r < kPreRounds; ++r) {
-    float acc = 0.f;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const f32x2 of = T::unpack2(o4[r][e]), df = T::unpack2(d4[r][e]);
-      acc = fmaf(of[0], df[0], acc);
-      acc = fmaf(of[1], df[1], acc);
-    }
-#pragma unroll
-    for (int k = LPR / 2; k >= 1; k >>= 1) acc += __shfl_xor(acc, k);
-    const int64_t x = x0 + r * RPW;
-    if (x < n && sub == 0) {
-      const float l = a.lse[x];
-      a.ld[x] = make_float2(l == kNegInf ? __builtin_huge_valf() : l * kLog2e, acc);
-    }
-  }
 }
 
 // ---------------------------------------------------------------------------
@@ -189,10 +141,26 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
       qreg[kk] ^= qflip;
       doreg[kk] = qvalid ? *(const u32x4*)(a.dout + rowo + 16 * kk) : (u32x4){0, 0, 0, 0};
     }
+    // Di = <dout_i, out_i> (each half of the row on one lane half, summed in
+    // a fixed order) and the lse in base 2, stored for the dk/dv kernel.
+    float acc = 0.f;
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) {
+      const u32x4 o4 = qvalid ? *(const u32x4*)(a.out + rowo + 16 * kk) : (u32x4){0, 0, 0, 0};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const f32x2 of = T::unpack2(o4[e]), df = T::unpack2(doreg[kk][e]);
+        acc = fmaf(of[0], df[0], acc);
+        acc = fmaf(of[1], df[1], acc);
+      }
+    }
+    acc += __shfl_xor(acc, 32);
     if (qvalid) {
-      const float2 ld = a.ld[((size_t)b * a.H_q + h) * a.S_q + qi];
-      l2 = ld.x;
-      di = ld.y;
+      const size_t x = ((size_t)b * a.H_q + h) * a.S_q + qi;
+      const float l = a.lse[x];
+      l2 = l == kNegInf ? __builtin_huge_valf() : l * kLog2e;
+      di = acc;
+      if (g == 0) a.ld[x] = make_float2(l2, di);
     }
   }
   const float sc2 = a.scale2;

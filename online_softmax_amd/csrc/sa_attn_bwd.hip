@@ -2,8 +2,8 @@
 //
 // Host code around the kernels of backward.hpp: validate (host_logic.cpp, no
 // HIP call), pick the template instance for {dtype, D, causal, mask, ALiBi},
-// launch the per-row pre-pass, the dq kernel and the dk/dv kernel on the
-// caller's stream.  This file is compiled on its own, with MFMA results kept
+// launch the dq kernel (which also forms each row's Di and base-2 lse for the
+// next kernel) and the dk/dv kernel on the caller's stream.  This file is compiled on its own, with MFMA results kept
 // in ordinary vector registers: the dk/dv kernel holds both gradient blocks
 // and its key/value rows live across the whole sweep, and letting the
 // compiler place MFMA results in accumulation registers made it move those
@@ -29,9 +29,6 @@ void launch_bwd_main(const BwdArgs& args, hipStream_t st) {
 
 template <class T, int D>
 void dispatch_bwd(const BwdArgs& args, bool causal, bool mask, bool alibi, hipStream_t st) {
-  const int64_t rows = (int64_t)args.B * args.H_q * args.S_q;
-  constexpr int rpb = pre_rows_per_block<D>();
-  if (rows > 0) hipLaunchKernelGGL((bwd_pre_kernel<T, D>), dim3((unsigned)((rows + rpb - 1) / rpb)), dim3(256), 0, st, args);
   const int key = (causal ? 4 : 0) | (mask ? 2 : 0) | (alibi ? 1 : 0);
   switch (key) {
     case 0: launch_bwd_main<T, D, false, false, false>(args, st); break;
