@@ -327,7 +327,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
 // the KV head.
 template <class T, int D, bool CAUSAL, bool MASK, bool ALIBI>
 __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdArgs a) {
-  constexpr int NW = 4, BK = 32 * NW, BQ = 32, NS = 2;
+  constexpr int NW = 4, BK = 32 * NW, BQ = 32, NS = 3;
   constexpr int KK = D / 16, DB = D / 32;
   constexpr int NI = BQ * D * 2 / 1024;  // 1 KiB copies per tensor per tile (all by one wave each)
   // Q and dO tiles of one buffer side by side, so that a dO fragment is read
@@ -390,7 +390,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdArgs a) {
     const int gi = it / per_head, qt = qtile(it, gi);
     const int h = hk * a.G + gi;
     const int i0 = qt * BQ, rows = min(BQ, a.S_q - i0);
-    const int buf = it % NS;
+    const int buf = __builtin_amdgcn_readfirstlane(it % NS);
     if (w == 0 || w == 1) {
       const uint16_t* base = (w == 0 ? a.q : a.dout) + (((size_t)b * a.S_q + i0) * a.H_q + h) * D;
       const auto r = buffer_rsrc(base, (uint32_t)((rows - 1) * qrs * 2 + 2 * D));
@@ -456,16 +456,23 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdArgs a) {
   // ALiBi slope of the tile's query head, read when the head changes.
   int slope_head = -1;
   float slope_acc = 0.f;
+  // Three buffers, one barrier per tile: tile it + 2 is copied right after
+  // the barrier of tile it, into the buffer of tile it - 1, which every wave
+  // finished reading before that barrier; the copies of two tiles are in
+  // flight under each tile's work.
   if (niter > 0) issue(0);
+  if (niter > 1) issue(1);
   for (int it = 0; it < niter; ++it) {
+    // Tile it has landed once at most the copies of tile it + 1 (issued
+    // after it) are in flight.
     if (it + 1 < niter) {
-      issue(it + 1);
       if (w <= 1) wait_vmem_n<NI>();
       else if (w == 2) wait_vmem_n<1>();
     } else {
       wait_vmem();
     }
     __syncthreads();
+    if (it + 2 < niter) issue(it + 2);
     const int gi = it / per_head, qt = qtile(it, gi);
     const int h = hk * a.G + gi;
     const int i0 = qt * BQ;
@@ -473,9 +480,10 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdArgs a) {
     // a tile whose rows all end before the wave's first key is skipped.
     const bool active = !CAUSAL || i0 + BQ - 1 + off >= kw0;
     if (active) {
-      const uint16_t* qt_ = QOs[it % NS][0];
+      const int buf = __builtin_amdgcn_readfirstlane(it % NS);
+      const uint16_t* qt_ = QOs[buf][0];
       const uint16_t* ot_ = qt_ + BQ * D;
-      const float2* lt = Ls[it % NS];
+      const float2* lt = Ls[buf];
       if (ALIBI && gi != slope_head) {
         slope_head = gi;
         slope_acc = scalar_load_f32(a.slopes + __builtin_amdgcn_readfirstlane(h)) * a.alibi2;
@@ -569,7 +577,6 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdArgs a) {
         __builtin_amdgcn_sched_barrier(0);
       }
     }
-    __syncthreads();
   }
 
   if (kvalid) {
