@@ -215,16 +215,15 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
     }
 
   for (int t = 0; t < nt; ++t) {
-    // Tile t is in buffer t % 2; issue tile t+1 into the other one, which
-    // every wave finished reading before the barrier that ended t-1.
+    // Tile t is in buffer t % 2, and its copies are the only ones in flight.
+    // After the barrier every wave has finished tile t - 1, so tile t + 1
+    // goes into that buffer while tile t is worked on: one barrier per tile.
+    wait_vmem();
+    __syncthreads();
     if (t + 1 < nt) {
       issue(kb, Ks[(t + 1) % NS], t + 1);
       issue(vb, Vs[(t + 1) % NS], t + 1);
-      wait_vmem_n<2 * NI>();
-    } else {
-      wait_vmem();
     }
-    __syncthreads();
     if (t < ntw) {
       const uint16_t* kt = Ks[t % NS];
       const uint16_t* vt = Vs[t % NS];
@@ -305,7 +304,6 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
         }
       }
     }
-    __syncthreads();
   }
 
   if (qvalid) {
